@@ -1,0 +1,139 @@
+/*
+ * libptpc -- PTPC-FP8 linear-layer hot path for AMD MI355X (gfx950).
+ *
+ * The method: vLLM blog "PTPC-FP8: Boosting vLLM Performance on AMD ROCm"
+ * (2025-02-24), cited below as [PTPC].  FP8 weights and FP8 activations,
+ * one scale per token for the activations and one per output channel for
+ * the weights (§What is PTPC-FP8; §PTPC: a precision-targeted scheme), with
+ * the scales applied to the GEMM result on chip before it is written
+ * (§The solution: fusion; §Why this matters).  The FP8 format is OCP E4M3
+ * (largest finite value 448).
+ *
+ * Conventions shared by every call:
+ *   - Every buffer pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or keeps a pointer past the call.
+ *   - bf16 buffers are passed as void* holding bf16 bit patterns; E4M3
+ *     buffers as uint8_t* holding E4M3 bit patterns; scales are fp32.
+ *   - Matrices are row-major; leading dimensions (ld*) are in ELEMENTS.
+ *   - stream is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns without synchronising; calls are
+ *     thread-safe (no global mutable state).
+ *   - Arguments are validated on the host before anything is enqueued.  On
+ *     any error nothing is launched and no output is touched.  A failed
+ *     launch reports PTPC_ERR_HIP.  No call aborts or throws.
+ *   - Supported shapes (v1): T >= 0, Ci >= 0, Co >= 0 with Ci % 16 == 0 and
+ *     Co % 16 == 0; base pointers 16-byte aligned; bf16 pitches multiples of
+ *     8 elements and E4M3 pitches multiples of 16 (16-byte rows).  A zero
+ *     extent is a no-op returning PTPC_OK (except as noted for Ci == 0).
+ *     Anything else returns PTPC_ERR_UNSUPPORTED / PTPC_ERR_ALIGN.
+ *
+ * Quantization rule (readings taken where [PTPC] is silent):
+ *   Delta = amax / 448 in fp32 (an all-zero vector gets Delta = 1);
+ *   code  = E4M3(x / Delta), the fp32 quotient correctly rounded, then
+ *           rounded to the nearest E4M3 value, ties to even, saturating at
+ *           +-448, sign kept.
+ */
+#ifndef PTPC_H
+#define PTPC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PTPC_ABI_VERSION 1
+
+typedef enum {
+    PTPC_OK = 0,
+    PTPC_ERR_NULL = 1,        /* a required pointer is NULL                 */
+    PTPC_ERR_SHAPE = 2,       /* negative extent, or pitch below the extent */
+    PTPC_ERR_UNSUPPORTED = 3, /* shape outside the v1 contract above         */
+    PTPC_ERR_ALIGN = 4,       /* pointer or pitch not 16-byte aligned        */
+    PTPC_ERR_HIP = 5          /* the HIP runtime refused a launch            */
+} ptpc_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* ptpc_status_string(int status);
+
+/* PTPC_ABI_VERSION of the built library. */
+int ptpc_abi_version(void);
+
+/*
+ * Per-token activation quantization ([PTPC] §PTPC: a precision-targeted
+ * scheme, "per-token activation quantization"; §Understanding the figure,
+ * Delta_X of shape [T x 1]).
+ *   x   [T x Ci] bf16, pitch ldx (>= Ci)         -- read
+ *   qx  [T x Ci] E4M3 codes, pitch ldq (>= Ci)   -- written
+ *   dx  [T] fp32, dx[t] = max_k |x[t,k]| / 448 (1 for an all-zero row)
+ * Ci == 0 with T > 0 writes dx[t] = 1 and no codes.
+ */
+ptpc_status ptpc_quant_act(const void* x, int64_t T, int64_t Ci, int64_t ldx,
+                           uint8_t* qx, int64_t ldq, float* dx, void* stream);
+
+/*
+ * Size in bytes of the packed weight buffer for a [Ci x Co] weight:
+ * Co * roundup(Ci, 128).  Returns 0 for unsupported or empty shapes.
+ */
+size_t ptpc_weight_packed_bytes(int64_t Ci, int64_t Co);
+
+/*
+ * Per-output-channel weight quantization and prepacking ([PTPC]
+ * §PTPC: a precision-targeted scheme, "per-channel weight quantization",
+ * each weight column gets its own scale; §Understanding the figure,
+ * Delta_W of shape [1 x Co]; done once when the model loads, no
+ * pre-quantized checkpoint -- §TL;DR / §Getting started).
+ *   w         [Ci x Co] bf16, pitch ldw (>= Co)             -- read
+ *   w_packed  ptpc_weight_packed_bytes(Ci, Co) bytes         -- written
+ *             layout: E4M3 code of w[k][o] at byte o*Kp + k with
+ *             Kp = roundup(Ci, 128), zero codes for Ci <= k < Kp
+ *             (the K-contiguous order the GEMM's MFMA B operand reads).
+ *   dw        [Co] fp32, dw[o] = max_k |w[k,o]| / 448 (1 for a zero column);
+ *             also used as the column-amax scratch during the call.
+ */
+ptpc_status ptpc_quant_weight(const void* w, int64_t Ci, int64_t Co, int64_t ldw,
+                              void* w_packed, float* dw, void* stream);
+
+/*
+ * Inverse of the packing, for tests and inspection: qw [Ci x Co] E4M3 codes,
+ * row-major with pitch Co, qw[k][o] = code of w[k][o].
+ */
+ptpc_status ptpc_unpack_weight(const void* w_packed, int64_t Ci, int64_t Co,
+                               uint8_t* qw, void* stream);
+
+/*
+ * Fused PTPC-FP8 GEMM ([PTPC] §The solution: fusion -- the scaled GEMM that
+ * takes the token scales and channel scales; §Why this matters -- scaling
+ * happens on chip before the result is written):
+ *   out[t,o] = bf16( (acc[t,o] * dx[t]) * dw[o] ),
+ *   acc[t,o] = sum_k E4M3(qx[t,k]) * E4M3(qw[k,o])   (FP8 MFMA, fp32 accumulate)
+ *   qx [T x Ci] pitch ldq; dx [T]; w_packed / dw from ptpc_quant_weight;
+ *   out [T x Co] bf16, pitch ldo (>= Co), written once.
+ * The fp32 products are rounded to bf16 with round-to-nearest-even.
+ */
+ptpc_status ptpc_gemm(const uint8_t* qx, int64_t ldq, const float* dx,
+                      const void* w_packed, const float* dw, int64_t T,
+                      int64_t Ci, int64_t Co, void* out, int64_t ldo,
+                      void* stream);
+
+/* Workspace needed by ptpc_gemm_unfused: 4 * T * Co bytes (fp32 [T x Co]). */
+size_t ptpc_gemm_unfused_workspace_bytes(int64_t T, int64_t Co);
+
+/*
+ * The naive two-step form ([PTPC] §The challenge: two-step vs fused): step 1
+ * is the same FP8 GEMM writing the unscaled fp32 result to `workspace`
+ * ([T x Co], pitch Co, caller-allocated, at least
+ * ptpc_gemm_unfused_workspace_bytes(T, Co) bytes); step 2 reads it back and
+ * writes out = bf16((ws * dx[t]) * dw[o]).  Same arguments and result as
+ * ptpc_gemm (bit-identical output), kept for comparison.
+ */
+ptpc_status ptpc_gemm_unfused(const uint8_t* qx, int64_t ldq, const float* dx,
+                              const void* w_packed, const float* dw, int64_t T,
+                              int64_t Ci, int64_t Co, void* out, int64_t ldo,
+                              float* workspace, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PTPC_H */

@@ -1,0 +1,175 @@
+"""Python binding of libptpc, the PTPC-FP8 hot path for MI355X (gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libptpc.so`` behind the C ABI declared in ``include/ptpc.h``.  PyTorch
+provides device memory and the current stream; nothing here computes.  If
+the library has not been built, every call raises -- there is no fallback.
+
+Tensors: bf16 inputs as ``torch.bfloat16``; E4M3 codes as ``torch.uint8``
+(view as ``torch.float8_e4m3fn`` if wanted); scales ``torch.float32``.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # must load before libptpc so both share torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libptpc.so")
+
+_STATUS = {
+    0: "PTPC_OK", 1: "PTPC_ERR_NULL", 2: "PTPC_ERR_SHAPE", 3: "PTPC_ERR_UNSUPPORTED",
+    4: "PTPC_ERR_ALIGN", 5: "PTPC_ERR_HIP",
+}
+
+# Every symbol include/ptpc.h declares.
+EXPORTS = (
+    "ptpc_status_string", "ptpc_abi_version", "ptpc_quant_act", "ptpc_weight_packed_bytes",
+    "ptpc_quant_weight", "ptpc_unpack_weight", "ptpc_gemm",
+    "ptpc_gemm_unfused_workspace_bytes", "ptpc_gemm_unfused",
+)
+
+_lib = None
+
+
+class PtpcError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)}")
+
+
+def lib():
+    """The loaded libptpc.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m scaled_gemm_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        L.ptpc_status_string.restype = ctypes.c_char_p
+        L.ptpc_status_string.argtypes = [ctypes.c_int]
+        L.ptpc_abi_version.restype = ctypes.c_int
+        L.ptpc_abi_version.argtypes = []
+        L.ptpc_quant_act.restype = ctypes.c_int
+        L.ptpc_quant_act.argtypes = [P, I, I, I, P, I, P, P]
+        L.ptpc_weight_packed_bytes.restype = S
+        L.ptpc_weight_packed_bytes.argtypes = [I, I]
+        L.ptpc_quant_weight.restype = ctypes.c_int
+        L.ptpc_quant_weight.argtypes = [P, I, I, I, P, P, P]
+        L.ptpc_unpack_weight.restype = ctypes.c_int
+        L.ptpc_unpack_weight.argtypes = [P, I, I, P, P]
+        L.ptpc_gemm.restype = ctypes.c_int
+        L.ptpc_gemm.argtypes = [P, I, P, P, P, I, I, I, P, I, P]
+        L.ptpc_gemm_unfused_workspace_bytes.restype = S
+        L.ptpc_gemm_unfused_workspace_bytes.argtypes = [I, I]
+        L.ptpc_gemm_unfused.restype = ctypes.c_int
+        L.ptpc_gemm_unfused.argtypes = [P, I, P, P, P, I, I, I, P, I, P, P]
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise PtpcError(fn, status)
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+
+
+def _matrix(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != 2 or (t.numel() > 0 and t.stride(1) != 1):
+        raise ValueError(f"{name}: expected a 2-D tensor with unit column stride")
+    return t.shape[0], t.shape[1], max(t.stride(0), t.shape[1])
+
+
+def packed_bytes(Ci: int, Co: int) -> int:
+    return int(lib().ptpc_weight_packed_bytes(Ci, Co))
+
+
+def workspace_bytes(T: int, Co: int) -> int:
+    return int(lib().ptpc_gemm_unfused_workspace_bytes(T, Co))
+
+
+@dataclass
+class PackedWeight:
+    """A weight quantized once: packed E4M3 codes plus its per-column scales."""
+    data: torch.Tensor     # uint8 [packed_bytes(Ci, Co)]
+    dw: torch.Tensor       # float32 [Co]
+    Ci: int
+    Co: int
+
+
+def quant_act(x, qx=None, dx=None, stream=None):
+    """Per-token FP8 quantization of bf16 X [T, Ci] -> (codes uint8 [T, Ci], dx fp32 [T])."""
+    T, Ci, ldx = _matrix(x, torch.bfloat16, "x")
+    if qx is None:
+        qx = torch.empty((T, Ci), dtype=torch.uint8, device=x.device)
+    if dx is None:
+        dx = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _, _, ldq = _matrix(qx, torch.uint8, "qx")
+    _check("ptpc_quant_act", lib().ptpc_quant_act(_ptr(x), T, Ci, ldx, _ptr(qx), ldq, _ptr(dx),
+                                                  _stream(stream)))
+    return qx, dx
+
+
+def quant_weight(w, out: PackedWeight = None, stream=None) -> PackedWeight:
+    """Per-output-channel FP8 quantization + MFMA prepack of bf16 W [Ci, Co]."""
+    Ci, Co, ldw = _matrix(w, torch.bfloat16, "w")
+    if out is None:
+        out = PackedWeight(torch.empty((packed_bytes(Ci, Co),), dtype=torch.uint8, device=w.device),
+                           torch.empty((Co,), dtype=torch.float32, device=w.device), Ci, Co)
+    _check("ptpc_quant_weight", lib().ptpc_quant_weight(_ptr(w), Ci, Co, ldw, _ptr(out.data),
+                                                        _ptr(out.dw), _stream(stream)))
+    return out
+
+
+def unpack_weight(pw: PackedWeight, stream=None):
+    """E4M3 codes of the weight back in [Ci, Co] order (for tests)."""
+    qw = torch.empty((pw.Ci, pw.Co), dtype=torch.uint8, device=pw.data.device)
+    _check("ptpc_unpack_weight", lib().ptpc_unpack_weight(_ptr(pw.data), pw.Ci, pw.Co, _ptr(qw),
+                                                          _stream(stream)))
+    return qw
+
+
+def gemm(qx, dx, pw: PackedWeight, out=None, stream=None):
+    """Fused PTPC GEMM: bf16 [T, Co] = ((qx @ qw) * dx[:, None]) * dw[None, :]."""
+    T, Ci, ldq = _matrix(qx, torch.uint8, "qx")
+    if Ci != pw.Ci:
+        raise ValueError(f"qx has Ci={Ci}, weight has Ci={pw.Ci}")
+    if out is None:
+        out = torch.empty((T, pw.Co), dtype=torch.bfloat16, device=qx.device)
+    _, _, ldo = _matrix(out, torch.bfloat16, "out")
+    _check("ptpc_gemm", lib().ptpc_gemm(_ptr(qx), ldq, _ptr(dx), _ptr(pw.data), _ptr(pw.dw), T,
+                                        Ci, pw.Co, _ptr(out), ldo, _stream(stream)))
+    return out
+
+
+def gemm_unfused(qx, dx, pw: PackedWeight, out=None, workspace=None, stream=None):
+    """Two-step form: fp32 GEMM result to `workspace`, then a rescale pass."""
+    T, Ci, ldq = _matrix(qx, torch.uint8, "qx")
+    if Ci != pw.Ci:
+        raise ValueError(f"qx has Ci={Ci}, weight has Ci={pw.Ci}")
+    if out is None:
+        out = torch.empty((T, pw.Co), dtype=torch.bfloat16, device=qx.device)
+    if workspace is None:
+        workspace = torch.empty((T, pw.Co), dtype=torch.float32, device=qx.device)
+    _, _, ldo = _matrix(out, torch.bfloat16, "out")
+    _check("ptpc_gemm_unfused",
+           lib().ptpc_gemm_unfused(_ptr(qx), ldq, _ptr(dx), _ptr(pw.data), _ptr(pw.dw), T, Ci,
+                                   pw.Co, _ptr(out), ldo, _ptr(workspace), _stream(stream)))
+    return out
+
+
+def linear(x, pw: PackedWeight, stream=None):
+    """Per-token quantization of X followed by the fused GEMM (one layer's forward)."""
+    qx, dx = quant_act(x, stream=stream)
+    return gemm(qx, dx, pw, stream=stream)

@@ -1,0 +1,30 @@
+// Internal launchers of libptpc (host side).  Every launcher only enqueues
+// kernels on the given stream and returns hipGetLastError(); argument
+// validation happens before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ptpc {
+
+// K extent of the packed weight: whole 128-byte K tiles.
+inline int64_t round_up_k(int64_t Ci) { return (Ci + 127) / 128 * 128; }
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t Ci, int64_t ldx,
+                            uint8_t* qx, int64_t ldq, float* dx, hipStream_t s);
+
+hipError_t launch_quant_weight(const uint16_t* w, int64_t Ci, int64_t Co, int64_t ldw,
+                               uint8_t* packed, float* dw, hipStream_t s);
+
+hipError_t launch_unpack_weight(const uint8_t* packed, int64_t Ci, int64_t Co, uint8_t* qw,
+                                hipStream_t s);
+
+// fp32_out == nullptr: fused epilogue writing bf16 `out`.
+// fp32_out != nullptr: the GEMM stores unscaled fp32 sums there ([T x Co],
+// pitch Co), then a rescale kernel writes bf16 `out`.
+hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
+                       const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
+                       int64_t ldo, float* fp32_out, hipStream_t s);
+
+}  // namespace ptpc

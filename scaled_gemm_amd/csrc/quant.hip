@@ -1,0 +1,325 @@
+// Per-token activation quantization and per-channel weight quantization +
+// prepacking for gfx950.
+//
+// Method: vLLM blog "PTPC-FP8: Boosting vLLM Performance on AMD ROCm",
+// §PTPC: a precision-targeted scheme (one scale per token, one per weight
+// column) and §Understanding the figure (Delta_X is [T x 1], Delta_W is
+// [1 x Co]).  Scale = amax / 448 (1 for an all-zero vector); code =
+// OCP E4M3(x / scale), round to nearest even.
+//
+// Both quantizers are HBM-bound streams (2 bytes read, 1 byte written per
+// element).  The activation kernel keeps each row in registers between the
+// amax pass and the cast, so X is read from HBM exactly once.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace ptpc {
+
+// ---------------------------------------------------------------------------
+// quant_act: a group of G threads owns one row; each thread holds VPT
+// 16-byte vectors (8 bf16 each) of the row in registers.  Vector j of thread
+// g is chunk j*G + g, so a group's loads for one j are contiguous.
+// ---------------------------------------------------------------------------
+template <int G, int VPT>
+__global__ __launch_bounds__(256) void quant_act_kernel(
+    const uint16_t* __restrict__ x, int64_t T, int64_t Ci, int64_t ldx,
+    uint8_t* __restrict__ qx, int64_t ldq, float* __restrict__ dx) {
+    constexpr int ROWS = 256 / G;
+    __shared__ uint32_t red[256 / 64];
+    const int tid = threadIdx.x;
+    const int g = tid % G;
+    const int64_t t = (int64_t)blockIdx.x * ROWS + tid / G;
+    const bool row_ok = t < T;
+    const int64_t nchunk = Ci / 8;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (row_ok ? t : 0) * ldx);
+
+    uint4 v[VPT];
+    us2 m = {0, 0};
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int64_t c = (int64_t)j * G + g;
+        if (row_ok && c < nchunk) {
+            v[j] = xr[c];
+        } else {
+            v[j] = make_uint4(0, 0, 0, 0);
+        }
+        m = max2(m, abs_bits2(v[j].x));
+        m = max2(m, abs_bits2(v[j].y));
+        m = max2(m, abs_bits2(v[j].z));
+        m = max2(m, abs_bits2(v[j].w));
+    }
+    uint32_t amax_bits;
+    if constexpr (G <= 64) {
+        amax_bits = group_max_u32<G>(hmax(m));
+    } else {
+        uint32_t w = wave_max_u32(hmax(m));
+        if ((tid & 63) == 0) red[tid >> 6] = w;
+        __syncthreads();
+        amax_bits = 0;
+#pragma unroll
+        for (int i = 0; i < G / 64; ++i) {
+            uint32_t o = red[(tid / G) * (G / 64) + i];
+            amax_bits = amax_bits > o ? amax_bits : o;
+        }
+    }
+    if (!row_ok) return;
+    const float d = scale_from_amax(__uint_as_float(amax_bits << 16));
+    const Divisor dv = make_divisor(d);
+    uint2* qr = reinterpret_cast<uint2*>(qx + t * ldq);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const int64_t c = (int64_t)j * G + g;
+        if (c < nchunk) qr[c] = quantize8(v[j], dv);
+    }
+    if (g == 0) dx[t] = d;
+}
+
+// Rows longer than 256 threads x 16 vectors: amax pass, then a second read.
+__global__ __launch_bounds__(256) void quant_act_long_kernel(
+    const uint16_t* __restrict__ x, int64_t Ci, int64_t ldx,
+    uint8_t* __restrict__ qx, int64_t ldq, float* __restrict__ dx) {
+    __shared__ uint32_t red[4];
+    const int tid = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    const int64_t nchunk = Ci / 8;
+    const uint4* xr = reinterpret_cast<const uint4*>(x + t * ldx);
+    us2 m = {0, 0};
+    for (int64_t c = tid; c < nchunk; c += 256) {
+        uint4 v = xr[c];
+        m = max2(m, abs_bits2(v.x));
+        m = max2(m, abs_bits2(v.y));
+        m = max2(m, abs_bits2(v.z));
+        m = max2(m, abs_bits2(v.w));
+    }
+    uint32_t w = wave_max_u32(hmax(m));
+    if ((tid & 63) == 0) red[tid >> 6] = w;
+    __syncthreads();
+    uint32_t a = red[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) a = a > red[i] ? a : red[i];
+    const float d = scale_from_amax(__uint_as_float(a << 16));
+    const Divisor dv = make_divisor(d);
+    uint2* qr = reinterpret_cast<uint2*>(qx + t * ldq);
+    for (int64_t c = tid; c < nchunk; c += 256) qr[c] = quantize8(xr[c], dv);
+    if (tid == 0) dx[t] = d;
+}
+
+__global__ void fill_f32_kernel(float* __restrict__ p, int64_t n, float v) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+template <int G, int VPT>
+static hipError_t launch_act(const uint16_t* x, int64_t T, int64_t Ci, int64_t ldx,
+                             uint8_t* qx, int64_t ldq, float* dx, hipStream_t s) {
+    constexpr int ROWS = 256 / G;
+    const int64_t blocks = (T + ROWS - 1) / ROWS;
+    hipLaunchKernelGGL((quant_act_kernel<G, VPT>), dim3((unsigned)blocks), dim3(256), 0, s,
+                       x, T, Ci, ldx, qx, ldq, dx);
+    return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_act_g(int vpt, const uint16_t* x, int64_t T, int64_t Ci, int64_t ldx,
+                               uint8_t* qx, int64_t ldq, float* dx, hipStream_t s) {
+    switch (vpt) {
+        case 1: return launch_act<G, 1>(x, T, Ci, ldx, qx, ldq, dx, s);
+        case 2: return launch_act<G, 2>(x, T, Ci, ldx, qx, ldq, dx, s);
+        case 4: return launch_act<G, 4>(x, T, Ci, ldx, qx, ldq, dx, s);
+        case 8: return launch_act<G, 8>(x, T, Ci, ldx, qx, ldq, dx, s);
+        default: return launch_act<G, 16>(x, T, Ci, ldx, qx, ldq, dx, s);
+    }
+}
+
+static int pow2_ceil(int64_t v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t Ci, int64_t ldx,
+                            uint8_t* qx, int64_t ldq, float* dx, hipStream_t s) {
+    if (Ci == 0) {
+        hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s,
+                           dx, T, 1.0f);
+        return hipGetLastError();
+    }
+    const int64_t nchunk = Ci / 8;
+    // Aim for about 8 vectors per thread; groups of 16..256 threads per row.
+    int64_t G = pow2_ceil((nchunk + 7) / 8);
+    if (G < 16) G = 16;
+    if (G > 256) G = 256;
+    const int64_t per = (nchunk + G - 1) / G;
+    if (per > 16) {
+        hipLaunchKernelGGL(quant_act_long_kernel, dim3((unsigned)T), dim3(256), 0, s,
+                           x, Ci, ldx, qx, ldq, dx);
+        return hipGetLastError();
+    }
+    const int vpt = pow2_ceil(per);
+    switch (G) {
+        case 16: return launch_act_g<16>(vpt, x, T, Ci, ldx, qx, ldq, dx, s);
+        case 32: return launch_act_g<32>(vpt, x, T, Ci, ldx, qx, ldq, dx, s);
+        case 64: return launch_act_g<64>(vpt, x, T, Ci, ldx, qx, ldq, dx, s);
+        case 128: return launch_act_g<128>(vpt, x, T, Ci, ldx, qx, ldq, dx, s);
+        default: return launch_act_g<256>(vpt, x, T, Ci, ldx, qx, ldq, dx, s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// quant_weight.  W is [Ci x Co] row-major; the per-column amax runs down the
+// long K direction, so it is split over row blocks and merged with integer
+// atomicMax on the fp32 bit patterns (non-negative floats order like their
+// bits) held in dw; a second kernel turns amax into the scale in place; the
+// third quantizes and writes the K-contiguous packed layout through an LDS
+// transpose.
+// ---------------------------------------------------------------------------
+constexpr int kColsPerBlock = 512;   // 64 lanes x 8 columns
+
+__global__ void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void weight_colamax_kernel(
+    const uint16_t* __restrict__ w, int64_t Ci, int64_t Co, int64_t ldw,
+    int64_t rows_per_split, uint32_t* __restrict__ amax_bits) {
+    __shared__ us2 red[4][64][4];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t col0 = (int64_t)blockIdx.x * kColsPerBlock + lane * 8;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_split;
+    int64_t r1 = r0 + rows_per_split;
+    if (r1 > Ci) r1 = Ci;
+    us2 m0 = {0, 0}, m1 = {0, 0}, m2 = {0, 0}, m3 = {0, 0};
+    if (col0 < Co) {
+        for (int64_t r = r0 + wave; r < r1; r += 4) {
+            uint4 v = *reinterpret_cast<const uint4*>(w + r * ldw + col0);
+            m0 = max2(m0, abs_bits2(v.x));
+            m1 = max2(m1, abs_bits2(v.y));
+            m2 = max2(m2, abs_bits2(v.z));
+            m3 = max2(m3, abs_bits2(v.w));
+        }
+    }
+    red[wave][lane][0] = m0;
+    red[wave][lane][1] = m1;
+    red[wave][lane][2] = m2;
+    red[wave][lane][3] = m3;
+    __syncthreads();
+    if (wave == 0 && col0 < Co) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            us2 a = max2(max2(red[0][lane][q], red[1][lane][q]), max2(red[2][lane][q], red[3][lane][q]));
+            if (a.x) atomicMax(amax_bits + col0 + 2 * q, (uint32_t)a.x << 16);
+            if (a.y) atomicMax(amax_bits + col0 + 2 * q + 1, (uint32_t)a.y << 16);
+        }
+    }
+}
+
+__global__ void weight_scale_kernel(float* __restrict__ dw, int64_t Co) {
+    int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (o < Co) dw[o] = scale_from_amax(dw[o]);
+}
+
+// Tile: 128 rows of K x 64 columns.  Each thread loads 16 bytes (8 columns)
+// of one row per pass, quantizes them with its 8 column divisors and drops
+// the codes transposed into LDS; the tile then leaves as 64 packed rows of
+// 128 contiguous K bytes.
+constexpr int kPackK = 128;
+constexpr int kPackN = 64;
+constexpr int kPackPitch = kPackK + 16;   // keeps 16-byte alignment of rows
+
+__global__ __launch_bounds__(256) void weight_pack_kernel(
+    const uint16_t* __restrict__ w, int64_t Ci, int64_t Co, int64_t ldw,
+    const float* __restrict__ dw, uint8_t* __restrict__ packed, int64_t Kp) {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kPackN * kPackPitch];
+    const int tid = threadIdx.x;
+    const int cg = tid & 7;            // 8-column group within the tile
+    const int rr = tid >> 3;           // row within a 32-row pass
+    const int64_t o0 = (int64_t)blockIdx.x * kPackN;
+    const int64_t k0 = (int64_t)blockIdx.y * kPackK;
+    const int64_t col = o0 + cg * 8;
+    const bool col_ok = col < Co;      // Co % 16 == 0: 8-column groups are whole
+
+    Divisor dv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dv[j] = make_divisor(col_ok ? dw[col + j] : 1.0f);
+
+#pragma unroll
+    for (int p = 0; p < kPackK / 32; ++p) {
+        const int kl = p * 32 + rr;
+        const int64_t k = k0 + kl;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (col_ok && k < Ci) v = *reinterpret_cast<const uint4*>(w + k * ldw + col);
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            uint32_t c = cvt_e4m3x2<false>(divide(bf16lo_to_f32(wd[h]), dv[2 * h]),
+                                           divide(bf16hi_to_f32(wd[h]), dv[2 * h + 1]), 0u);
+            tile[(cg * 8 + 2 * h) * kPackPitch + kl] = (uint8_t)(c & 0xFF);
+            tile[(cg * 8 + 2 * h + 1) * kPackPitch + kl] = (uint8_t)((c >> 8) & 0xFF);
+        }
+    }
+    __syncthreads();
+    // 64 columns x 128 bytes = 512 vectors of 16 bytes: two per thread.
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int i = p * 256 + tid;
+        const int n = i >> 3;
+        const int c = i & 7;
+        if (o0 + n < Co) {
+            uint4 val = *reinterpret_cast<const uint4*>(tile + n * kPackPitch + c * 16);
+            *reinterpret_cast<uint4*>(packed + (o0 + n) * Kp + k0 + c * 16) = val;
+        }
+    }
+}
+
+hipError_t launch_quant_weight(const uint16_t* w, int64_t Ci, int64_t Co, int64_t ldw,
+                               uint8_t* packed, float* dw, hipStream_t s) {
+    const int64_t Kp = round_up_k(Ci);
+    uint32_t* amax_bits = reinterpret_cast<uint32_t*>(dw);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((Co + 255) / 256)), dim3(256), 0, s,
+                       amax_bits, Co);
+    if (Ci > 0) {
+        const int64_t colblocks = (Co + kColsPerBlock - 1) / kColsPerBlock;
+        int64_t splits = 2048 / colblocks;
+        if (splits < 1) splits = 1;
+        int64_t max_splits = (Ci + 31) / 32;    // at least 32 rows per split
+        if (splits > max_splits) splits = max_splits;
+        if (splits > 65535) splits = 65535;
+        int64_t rows_per_split = (Ci + splits - 1) / splits;
+        rows_per_split = (rows_per_split + 3) / 4 * 4;
+        splits = (Ci + rows_per_split - 1) / rows_per_split;
+        hipLaunchKernelGGL(weight_colamax_kernel, dim3((unsigned)colblocks, (unsigned)splits),
+                           dim3(256), 0, s, w, Ci, Co, ldw, rows_per_split, amax_bits);
+    }
+    hipLaunchKernelGGL(weight_scale_kernel, dim3((unsigned)((Co + 255) / 256)), dim3(256), 0, s,
+                       dw, Co);
+    if (Kp > 0) {
+        hipLaunchKernelGGL(weight_pack_kernel,
+                           dim3((unsigned)((Co + kPackN - 1) / kPackN), (unsigned)(Kp / kPackK)),
+                           dim3(256), 0, s, w, Ci, Co, ldw, dw, packed, Kp);
+    }
+    return hipGetLastError();
+}
+
+__global__ void unpack_kernel(const uint8_t* __restrict__ packed, int64_t Ci, int64_t Co,
+                              int64_t Kp, uint8_t* __restrict__ qw) {
+    const int64_t n = Ci * Co;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t k = i / Co, o = i - k * Co;
+        qw[i] = packed[o * Kp + k];
+    }
+}
+
+hipError_t launch_unpack_weight(const uint8_t* packed, int64_t Ci, int64_t Co, uint8_t* qw,
+                                hipStream_t s) {
+    const int64_t n = Ci * Co;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, packed, Ci, Co,
+                       round_up_k(Ci), qw);
+    return hipGetLastError();
+}
+
+}  // namespace ptpc

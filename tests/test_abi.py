@@ -1,0 +1,140 @@
+"""The C ABI of libptpc on the CPU: the library loads, exports every symbol
+include/ptpc.h declares, and rejects bad arguments before touching the GPU
+(no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "ptpc.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import scaled_gemm_amd as sg
+    return sg.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(ptpc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    import scaled_gemm_amd as sg
+    assert declared_functions() == sorted(sg.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    import scaled_gemm_amd as sg
+    out = subprocess.run(["nm", "-D", "--defined-only", sg.LIB_PATH], check=True,
+                         stdout=subprocess.PIPE, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings(L):
+    assert L.ptpc_abi_version() == 1
+    for s in range(6):
+        assert L.ptpc_status_string(s).startswith(b"PTPC_")
+    assert L.ptpc_status_string(99) == b"unknown ptpc_status"
+
+
+def test_size_queries(L):
+    assert L.ptpc_weight_packed_bytes(256, 512) == 512 * 256
+    assert L.ptpc_weight_packed_bytes(1040, 32) == 32 * 1152
+    assert L.ptpc_weight_packed_bytes(8, 16) == 0          # Ci not a multiple of 16
+    assert L.ptpc_weight_packed_bytes(0, 16) == 0
+    assert L.ptpc_gemm_unfused_workspace_bytes(3, 16) == 3 * 16 * 4
+    assert L.ptpc_gemm_unfused_workspace_bytes(0, 16) == 0
+
+
+# Aligned, non-NULL fake device addresses.  Validation must reject before any
+# HIP call, and the fault-injection path returns before any launch, so these
+# are never dereferenced.
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+C = ctypes.c_void_p(0x30000)
+D = ctypes.c_void_p(0x40000)
+E = ctypes.c_void_p(0x50000)
+MIS = ctypes.c_void_p(0x10008)
+NULL = None
+
+
+def test_quant_act_validation(L):
+    f = L.ptpc_quant_act
+    assert f(A, 0, 256, 256, B, 256, C, None) == 0                 # empty: no-op
+    assert f(A, -1, 256, 256, B, 256, C, None) == 2
+    assert f(A, 4, 256, 128, B, 256, C, None) == 2                 # ldx < Ci
+    assert f(A, 4, 256, 256, B, 128, C, None) == 2                 # ldq < Ci
+    assert f(A, 4, 24, 24, B, 32, C, None) == 3                    # Ci % 16
+    assert f(NULL, 4, 256, 256, B, 256, C, None) == 1
+    assert f(A, 4, 256, 256, NULL, 256, C, None) == 1
+    assert f(A, 4, 256, 256, B, 256, NULL, None) == 1
+    assert f(MIS, 4, 256, 256, B, 256, C, None) == 4
+    assert f(A, 4, 256, 260, B, 256, C, None) == 4                 # pitch not 16 B
+    assert f(A, 4, 256, 256, B, 264, C, None) == 4
+
+
+def test_quant_weight_validation(L):
+    f = L.ptpc_quant_weight
+    assert f(A, 256, 0, 0, B, C, None) == 0
+    assert f(A, 256, 512, 500, B, C, None) == 2
+    assert f(A, 250, 512, 512, B, C, None) == 3
+    assert f(A, 256, 520, 520, B, C, None) == 3
+    assert f(NULL, 256, 512, 512, B, C, None) == 1
+    assert f(A, 256, 512, 512, NULL, C, None) == 1
+    assert f(A, 256, 512, 512, B, NULL, None) == 1
+    assert f(A, 256, 512, 512, MIS, C, None) == 4
+    assert L.ptpc_unpack_weight(NULL, 256, 512, B, None) == 1
+    assert L.ptpc_unpack_weight(A, 256, 500, B, None) == 3
+
+
+def test_gemm_validation(L):
+    for unfused in (False, True):
+        def f(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, ws=D):
+            if unfused:
+                return L.ptpc_gemm_unfused(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, ws, None)
+            return L.ptpc_gemm(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, None)
+        assert f(A, 256, B, C, D, 0, 256, 512, E, 512) == 0
+        assert f(A, 256, B, C, D, 4, 256, 512, E, 500) == 2
+        assert f(A, 100, B, C, D, 4, 256, 512, E, 512) == 2
+        assert f(A, 256, B, C, D, 4, 256, 500, E, 512) == 3
+        assert f(NULL, 256, B, C, D, 4, 256, 512, E, 512) == 1
+        assert f(A, 256, NULL, C, D, 4, 256, 512, E, 512) == 1
+        assert f(A, 256, B, NULL, D, 4, 256, 512, E, 512) == 1
+        assert f(A, 256, B, C, NULL, 4, 256, 512, E, 512) == 1
+        assert f(A, 256, B, C, D, 4, 256, 512, NULL, 512) == 1
+        assert f(MIS, 256, B, C, D, 4, 256, 512, E, 512) == 4
+        assert f(A, 256, B, C, D, 4, 256, 512, E, 516) == 4
+    assert L.ptpc_gemm_unfused(A, 256, B, C, D, 4, 256, 512, E, 512, NULL, None) == 1
+    assert L.ptpc_gemm_unfused(A, 256, B, C, D, 4, 256, 512, E, 512, MIS, None) == 4
+
+
+def test_forced_launch_failure_reports_hip_error():
+    """PTPC_FAULT=launch makes every launching call return PTPC_ERR_HIP from
+    the host, without a GPU; checked in a child process so the setting does
+    not leak into other tests."""
+    code = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+import scaled_gemm_amd as sg
+L = sg.lib()
+A, B, C, D, E = (ctypes.c_void_p(v) for v in (0x10000, 0x20000, 0x30000, 0x40000, 0x50000))
+r = [L.ptpc_quant_act(A, 4, 256, 256, B, 256, C, None),
+     L.ptpc_quant_weight(A, 256, 512, 512, B, C, None),
+     L.ptpc_unpack_weight(A, 256, 512, B, None),
+     L.ptpc_gemm(A, 256, B, C, D, 4, 256, 512, E, 512, None),
+     L.ptpc_gemm_unfused(A, 256, B, C, D, 4, 256, 512, E, 512, D, None),
+     L.ptpc_quant_act(A, 0, 256, 256, B, 256, C, None)]
+print(r)
+assert r == [5, 5, 5, 5, 5, 0], r
+""" % ROOT
+    env = dict(os.environ, PTPC_FAULT="launch", HIP_VISIBLE_DEVICES="")
+    subprocess.run(["python", "-c", code], check=True, env=env)
