@@ -1,0 +1,263 @@
+"""Benchmark of the PTPC-FP8 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 70b_down]
+
+One step = every stage of the path over one batch of resident synthetic
+input: per-channel weight quantization + prepack, per-token activation
+quantization, the fused FP8 GEMM, and the two-step (unfused) GEMM.  Each
+stage is bracketed by HIP events on the stream it runs on, so per-kernel
+averages come from the timed region itself.
+
+Prints one JSON line.  `value` is whole-step throughput: the FP8 contraction
+work of the step (two GEMMs, 2*T*Ci*Co flops each) divided by the step time.
+`roofline` is the fused GEMM against the dense FP8 MFMA peak; `quant_act`
+carries the activation quantizer against HBM bandwidth; `cpu_baseline` is
+the CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fused_70b_down_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="70b_down")
+    p.add_argument("--layer", default=None, help="70b_sweep layer")
+    p.add_argument("--T", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--only", default=None,
+                   help="comma list of stages to run (profiling); default all")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="run a plain device copy of this many MiB (3x) before timing, "
+                        "as the reference kernel for HBM byte counters")
+    return p.parse_args()
+
+
+def gemm_source_hash():
+    src = os.path.join(ROOT, "scaled_gemm_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per fused-GEMM launch from rocprofv3 FETCH_SIZE/WRITE_SIZE,
+    only if the counters were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(x_bits, w_bits, target_s):
+    """The CPU oracle (as it stands) on the first R token rows with the whole
+    weight: quantize, contract exactly, scale.  The oracle spreads rows over
+    its threads, so R is a multiple of the thread count, grown until about
+    target_s seconds of CPU work."""
+    import numpy as np
+    import oracle
+    Ci, Co = w_bits.shape
+    nthr = oracle.num_threads()
+    t0 = time.perf_counter()
+    qw, dw = oracle.quant_weight(w_bits)
+    t_w = time.perf_counter() - t0
+
+    def rows(R):
+        t0 = time.perf_counter()
+        qx, dx = oracle.quant_act(np.ascontiguousarray(x_bits[:R]))
+        oracle.apply_scales(oracle.gemm_exact(qx, qw), dx, dw)
+        return time.perf_counter() - t0
+
+    R = min(nthr, x_bits.shape[0])
+    t_g = rows(R)
+    reps = int((target_s - t_w - t_g) / max(t_g, 1e-6))
+    if reps >= 1 and R < x_bits.shape[0]:
+        R = min(x_bits.shape[0], R * (reps + 1))
+        t_g = rows(R)
+    total = t_w + t_g
+    flops = 2.0 * R * Ci * Co
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": min(nthr, R),
+            "kind": "oracle",
+            "sample": (f"first {R} token rows of the workload with its whole weight: "
+                       f"quant_weight [{Ci}x{Co}] + quant_act [{R}x{Ci}] + exact GEMM "
+                       f"[{R}x{Ci}]x[{Ci}x{Co}] + scales; {total:.1f} s wall "
+                       f"(weight quantization {t_w:.1f} s); {nthr} OpenMP threads")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import scaled_gemm_amd as sg
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sg.lib()
+
+    if args.workload == "70b_sweep":
+        shape, x_bits, w_bits = workloads.make("70b_sweep", T=args.T or 8192,
+                                               layer=args.layer or "gate_up")
+    else:
+        shape, x_bits, w_bits = workloads.make(args.workload, T=args.T)
+    T, Ci, Co = shape.T, shape.Ci, shape.Co
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # outputs allocated once, outside the timed region
+    qx = torch.empty((T, Ci), dtype=torch.uint8, device=dev)
+    dx = torch.empty((T,), dtype=torch.float32, device=dev)
+    pw = sg.PackedWeight(torch.empty((sg.packed_bytes(Ci, Co),), dtype=torch.uint8, device=dev),
+                         torch.empty((Co,), dtype=torch.float32, device=dev), Ci, Co)
+    out = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
+    out2 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((T, Co), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    stages = ["quant_weight", "quant_act", "gemm_fused", "gemm_unfused"]
+    run = set(args.only.split(",")) if args.only else set(stages)
+    unknown = run - set(stages)
+    if unknown:
+        raise SystemExit(f"unknown stages {sorted(unknown)}")
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        if "quant_weight" in run:
+            sg.quant_weight(w, out=pw)
+        mark(1)
+        if "quant_act" in run:
+            sg.quant_act(x, qx=qx, dx=dx)
+        mark(2)
+        if "gemm_fused" in run:
+            sg.gemm(qx, dx, pw, out=out)
+        mark(3)
+        if "gemm_unfused" in run:
+            sg.gemm_unfused(qx, dx, pw, out=out2, workspace=ws)
+        mark(4)
+
+    # inputs of the GEMMs exist even when their producers are not timed
+    sg.quant_weight(w, out=pw)
+    sg.quant_act(x, qx=qx, dx=dx)
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per_stage = {s: [] for s in stages}
+    for ev in events:
+        for i, s in enumerate(stages):
+            per_stage[s].append(ev[i].elapsed_time(ev[i + 1]))
+    avg = {s: float(np.mean(v)) for s, v in per_stage.items()}
+    med = {s: float(np.median(v)) for s, v in per_stage.items()}
+
+    gemm_flops = 2.0 * T * Ci * Co
+    act_bytes = 3.0 * T * Ci + 4.0 * T
+    w_bytes = 3.0 * Ci * Co + 4.0 * Co
+    fused_min_bytes = T * Ci + Ci * Co + 2.0 * T * Co + 4.0 * (T + Co)
+    ms_per_step = elapsed * 1e3 / args.steps
+    n_gemms = ("gemm_fused" in run) + ("gemm_unfused" in run)
+    value = n_gemms * gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    def rate(work, stage, scale):
+        return work / (avg[stage] * 1e-3) / scale if stage in run else float("nan")
+
+    fused_tflops = rate(gemm_flops, "gemm_fused", 1e12)
+    unfused_tflops = rate(gemm_flops, "gemm_unfused", 1e12)
+    act_gbs = rate(act_bytes, "quant_act", 1e9)
+    w_gbs = rate(w_bytes, "quant_weight", 1e9)
+    traffic = measured_traffic(shape.name)
+
+    result = {
+        "metric": "ptpc_gemm TFLOP/s (% FP8 MFMA peak); quant_act GB/s (% HBM) on 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded, Llama-3.1-70B/8B-shaped linear layers with outlier channels)",
+        "config": {
+            "workload": shape.name, "T": T, "Ci": Ci, "Co": Co,
+            "x": f"bf16 [{T}x{Ci}]", "w": f"bf16 [{Ci}x{Co}]", "out": f"bf16 [{T}x{Co}]",
+            "step": " + ".join(s for s in stages if s in run),
+            "value_work": f"{n_gemms} GEMMs x 2*T*Ci*Co flops per step",
+        },
+        "roofline": {
+            "kernel": "ptpc_gemm (fused)",
+            "bound": "mfma",
+            "achieved": round(fused_tflops, 1),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fused_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_min_bytes": fused_min_bytes,
+            "avg_launch_ms": round(avg["gemm_fused"], 4),
+        },
+        "quant_act": {
+            "bound": "hbm", "achieved": round(act_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(act_gbs / PEAK_HBM_GBS, 4), "avg_launch_ms": round(avg["quant_act"], 4),
+            "bytes_per_launch": act_bytes,
+        },
+        "stages_ms_avg": {k: round(v, 4) for k, v in avg.items()},
+        "stages_ms_median": {k: round(v, 4) for k, v in med.items()},
+        "quant_weight_gbs": round(w_gbs, 1),
+        "gemm_unfused_tflops": round(unfused_tflops, 1),
+        "fused_over_unfused": (round(avg["gemm_unfused"] / avg["gemm_fused"], 3)
+                               if {"gemm_fused", "gemm_unfused"} <= run else None),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

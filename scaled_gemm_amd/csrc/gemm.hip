@@ -15,77 +15,128 @@
 // and B tiles are both "rows of 128 K bytes" and both MFMA operands are read
 // from LDS the same way: lane l takes row l % 32 of a 32-row slab and 32
 // consecutive K bytes starting at 32 * (l / 32) within a 64-byte K step.
-// Each LDS row is 128 bytes = 8 chunks of 16 bytes, stored at chunk
-// position c ^ swz(row) so that the 32 rows one MFMA operand read touches
-// fall on different banks.
+//
+// Pipeline: tiles move HBM/L2 -> LDS with buffer_load_dwordx4 ... lds (no
+// staging registers, no ds_write); the buffer descriptor's range check
+// turns rows past T / Co and K past Ci into zeros.  LDS holds two stages;
+// while the MFMAs consume stage k, the loads for stage k+1 are in flight.
+// One LDS row is 128 bytes = 8 chunks of 16 bytes; chunk c of row r is
+// stored at slot c ^ swz(r), so the 32 rows an operand read touches spread
+// over the banks.  A load instruction fills 1 KB of LDS (64 lanes x 16 B,
+// i.e. 8 rows), so each lane fetches the global chunk that belongs in its
+// fixed LDS slot.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace ptpc {
 
-constexpr int BK = 128;
+constexpr int BK = 64;          // K bytes per pipeline stage (one MFMA K step)
+constexpr int NSTAGE = 4;       // LDS ring depth
+constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
-__device__ __forceinline__ int swz(int row) { return row & 7; }
+// Chunk slot of logical 16-byte chunk c in LDS row r.  A row is 64 bytes
+// (4 chunks); an operand read has 16 consecutive rows of one logical chunk in
+// flight per LDS cycle on the 64-bank LDS, and rows r, r+4, r+8, r+12 share
+// banks unless their slots differ.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kBufferDword3);
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// the fence would wait for every load in flight into LDS (vmcnt 0), which
+// would drain the prefetch ring.  Callers wait for exactly the fills they
+// need with wait_counts first; the memory clobber keeps the compiler from
+// moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt with vmcnt <= VM and lgkmcnt <= LGKM (expcnt not waited on).
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_counts() {
+    static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
 
 template <int BM, int BN, int WM, int WN, bool FUSED>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
     const uint8_t* __restrict__ wp, int64_t Kp, const float* __restrict__ dw,
     int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo) {
-    constexpr int NT = WM * WN * 64;
+    constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MT = WTM / 32, NTL = WTN / 32;
-    constexpr int AV = BM * 8 / NT;      // 16-byte vectors of the A tile per thread
-    constexpr int BV = BN * 8 / NT;
-    static_assert(AV * NT == BM * 8 && BV * NT == BN * 8, "tile/threads mismatch");
-    constexpr int TILE_VECS = (BM + BN) * 8;
-    __shared__ uint4 smem[2 * TILE_VECS];
+    constexpr int ROWS_PER_BLK = 1024 / BK;                   // rows one load instruction fills
+    constexpr int A_BLK = BM / ROWS_PER_BLK, B_BLK = BN / ROWS_PER_BLK;
+    constexpr int A_PER_W = A_BLK / NW, B_PER_W = B_BLK / NW;
+    constexpr int DPW = A_PER_W + B_PER_W;                    // load instructions per wave per stage
+    static_assert(A_PER_W * NW == A_BLK && B_PER_W * NW == B_BLK, "tile/waves mismatch");
+    static_assert(2 * DPW < 64, "vmcnt range");
+    constexpr int A_BYTES = BM * BK;
+    constexpr int STAGE = (BM + BN) * BK;
+    // Distinct LDS objects per stage (not one array indexed by stage) so
+    // that the compiler can tell the stage being filled from the stage being
+    // read and does not wait for the fills before the reads.
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage2[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage3[STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int64_t nk = Kp / BK;
+    const int nks = (int)(Kp / BK);                           // K steps with data
 
-    uint4 ra[AV], rb[BV];
+    // Buffer descriptors based at this tile's first row; rows past the end
+    // and K past the data land beyond num_records and read as zero.
+    const int64_t a_rows = (T - m0 < BM) ? (T - m0) : BM;
+    const int64_t b_rows = (Co - n0 < BN) ? (Co - n0) : BN;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(qx + m0 * ldq, (uint32_t)(a_rows * ldq));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(wp + n0 * Kp, (uint32_t)(b_rows * Kp));
 
-    auto load_tile = [&](int64_t kt) {
-        const int64_t k0 = kt * BK;
+    // A load instruction fills ROWS_PER_BLK rows: lane L owns LDS row L/4,
+    // slot L%4, and fetches the logical chunk that belongs in that slot.
+    const int lrow = lane >> 2;
+    const int slot = lane & 3;
+    uint32_t a_off[A_PER_W], b_off[B_PER_W];
+    int a_chunk[A_PER_W];
 #pragma unroll
-        for (int p = 0; p < AV; ++p) {
-            const int i = tid + p * NT;
-            const int row = i >> 3, c = i & 7;
-            const int64_t gr = m0 + row;
-            const int64_t gk = k0 + c * 16;
-            ra[p] = (gr < T && gk < Ci)
-                        ? *reinterpret_cast<const uint4*>(qx + gr * ldq + gk)
-                        : make_uint4(0, 0, 0, 0);
+    for (int p = 0; p < A_PER_W; ++p) {
+        const int r = (wave + p * NW) * ROWS_PER_BLK + lrow;
+        const int c = slot ^ swz(r);
+        a_chunk[p] = c;
+        a_off[p] = (r < a_rows) ? (uint32_t)(r * ldq + c * 16) : kOutOfRange;
+    }
+#pragma unroll
+    for (int p = 0; p < B_PER_W; ++p) {
+        const int r = (wave + p * NW) * ROWS_PER_BLK + lrow;
+        const int c = slot ^ swz(r);
+        b_off[p] = (r < b_rows) ? (uint32_t)(r * Kp + c * 16) : kOutOfRange;
+    }
+
+    auto issue_stage = [&](int ks, uint8_t* sa) {
+        const int k0 = ks * BK;
+        uint8_t* sb = sa + A_BYTES;
+#pragma unroll
+        for (int p = 0; p < A_PER_W; ++p) {
+            const bool kin = (int64_t)(k0 + a_chunk[p] * 16) < Ci;
+            const uint32_t off = (a_off[p] != kOutOfRange && kin) ? a_off[p] + k0 : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_ptr_t)(sa + (wave + p * NW) * 1024), 16, off, 0, 0, 0);
         }
+        const bool kin_b = k0 < Kp;
 #pragma unroll
-        for (int p = 0; p < BV; ++p) {
-            const int i = tid + p * NT;
-            const int row = i >> 3, c = i & 7;
-            const int64_t gn = n0 + row;
-            rb[p] = (gn < Co) ? *reinterpret_cast<const uint4*>(wp + gn * Kp + k0 + c * 16)
-                              : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_tile = [&](int buf) {
-        uint4* sa = smem + buf * TILE_VECS;
-        uint4* sb = sa + BM * 8;
-#pragma unroll
-        for (int p = 0; p < AV; ++p) {
-            const int i = tid + p * NT;
-            const int row = i >> 3, c = i & 7;
-            sa[row * 8 + (c ^ swz(row))] = ra[p];
-        }
-#pragma unroll
-        for (int p = 0; p < BV; ++p) {
-            const int i = tid + p * NT;
-            const int row = i >> 3, c = i & 7;
-            sb[row * 8 + (c ^ swz(row))] = rb[p];
+        for (int p = 0; p < B_PER_W; ++p) {
+            const uint32_t off = (b_off[p] != kOutOfRange && kin_b) ? b_off[p] + k0 : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_ptr_t)(sb + (wave + p * NW) * 1024), 16, off, 0, 0, 0);
         }
     };
 
@@ -97,53 +148,111 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    if (nk > 0) {
-        load_tile(0);
-        store_tile(0);
-        __syncthreads();
-    }
     const int lr = lane & 31;
     const int lg = lane >> 5;
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = (int)(kt & 1);
-        if (kt + 1 < nk) load_tile(kt + 1);
-        const uint4* sa = smem + cur * TILE_VECS;
-        const uint4* sb = sa + BM * 8;
+    // MFMA operands: lane l reads row l%32 of a 32-row slab, logical chunks
+    // 2*(l/32) and 2*(l/32)+1 of the 64-byte K step.
+    int a_lo[MT], a_hi[MT], b_lo[NTL], b_hi[NTL];
 #pragma unroll
-        for (int s = 0; s < BK / 64; ++s) {
-            const int c0 = s * 4 + lg * 2;
-            v8i af[MT], bf[NTL];
+    for (int i = 0; i < MT; ++i) {
+        const int r = wm * WTM + i * 32 + lr;
+        a_lo[i] = r * BK + (((2 * lg) ^ swz(r)) << 4);
+        a_hi[i] = r * BK + (((2 * lg + 1) ^ swz(r)) << 4);
+    }
 #pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                const int row = wm * WTM + i * 32 + lr;
-                uint4 lo = sa[row * 8 + (c0 ^ swz(row))];
-                uint4 hi = sa[row * 8 + ((c0 + 1) ^ swz(row))];
-                af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                            (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            }
+    for (int j = 0; j < NTL; ++j) {
+        const int r = wn * WTN + j * 32 + lr;
+        b_lo[j] = A_BYTES + r * BK + (((2 * lg) ^ swz(r)) << 4);
+        b_hi[j] = A_BYTES + r * BK + (((2 * lg + 1) ^ swz(r)) << 4);
+    }
+    auto read_frags = [&](const uint8_t* st, v8i (&a)[MT], v8i (&b)[NTL]) {
 #pragma unroll
-            for (int j = 0; j < NTL; ++j) {
-                const int row = wn * WTN + j * 32 + lr;
-                uint4 lo = sb[row * 8 + (c0 ^ swz(row))];
-                uint4 hi = sb[row * 8 + ((c0 + 1) ^ swz(row))];
-                bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                            (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            }
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-#pragma unroll
-                for (int j = 0; j < NTL; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[i], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+        for (int i = 0; i < MT; ++i) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(st + a_lo[i]);
+            const uint4 hi = *reinterpret_cast<const uint4*>(st + a_hi[i]);
+            a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
-        if (kt + 1 < nk) store_tile(cur ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(st + b_lo[j]);
+            const uint4 hi = *reinterpret_cast<const uint4*>(st + b_hi[j]);
+            b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+    };
+    // One K step: its MFMAs, with the next step's operand reads and the
+    // loads that refill the just-freed stage threaded between them (the
+    // reads fill the other fragment registers).  Issuing the loads in one
+    // burst would hold back the first MFMA until the texture unit accepted
+    // them all.
+    constexpr int NMFMA = MT * NTL;
+    constexpr int NREAD = 2 * (MT + NTL);
+    auto step = [&](int s, const v8i (&a)[MT], const v8i (&b)[NTL], const uint8_t* nxt,
+                    v8i (&na)[MT], v8i (&nb)[NTL], uint8_t* refill) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NTL; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+        read_frags(nxt, na, nb);
+        issue_stage(s + NSTAGE, refill);
+        constexpr int NQ = NMFMA > NREAD ? NMFMA : NREAD;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            if (q < NMFMA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            if (q < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+            if (q < DPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Top of K step s: the stage s+1 fill has landed (two later stages may
+    // still be in flight) and every wave has read stage s into registers, so
+    // stage s%4 is free for the fill of step s+4 (issued inside step s).
+    auto top = [&]() {
+        wait_counts<2 * DPW, 0>();
+        lds_barrier();
+    };
+
+    // Ring of four stages; K steps past the data are filled with zeros (all
+    // offsets out of range) so the loop needs no branch; at most three extra
+    // zero steps are multiplied.  The loop is unrolled by four so every
+    // access names its stage.
+    v8i fa0[MT], fb0[NTL], fa1[MT], fb1[NTL];
+    if (nks > 0) {
+        issue_stage(0, stage0);
+        issue_stage(1, stage1);
+        issue_stage(2, stage2);
+        issue_stage(3, stage3);
+        wait_counts<3 * DPW, 15>();     // stage 0 landed
+        lds_barrier();
+        read_frags(stage0, fa0, fb0);
+        for (int s = 0; s < nks; s += NSTAGE) {
+            top();
+            step(s, fa0, fb0, stage1, fa1, fb1, stage0);
+            top();
+            step(s + 1, fa1, fb1, stage2, fa0, fb0, stage1);
+            top();
+            step(s + 2, fa0, fb0, stage3, fa1, fb1, stage2);
+            top();
+            step(s + 3, fa1, fb1, stage0, fa0, fb0, stage3);
+        }
+        wait_counts<0, 0>();            // no fill may land after the loop
+        lds_barrier();
     }
 
     // Epilogue.  Accumulator element e of a 32x32 tile in lane l sits at
     // row 8*(e/4) + 4*(l/32) + e%4, column l%32.
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
+        float sx[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+            sx[e] = (FUSED && row < T) ? dx[row] : 0.0f;
+        }
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
             const int64_t col = n0 + wn * WTN + j * 32 + lr;
@@ -154,7 +263,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(
                 const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
                 if (row >= T) continue;
                 if constexpr (FUSED) {
-                    const float v = (acc[i][j][e] * dx[row]) * sw;
+                    const float v = (acc[i][j][e] * sx[e]) * sw;
                     reinterpret_cast<uint16_t*>(out)[row * ldo + col] = f32_to_bf16_rne(v);
                 } else {
                     reinterpret_cast<float*>(out)[row * Co + col] = acc[i][j][e];
@@ -179,11 +288,12 @@ __global__ __launch_bounds__(256) void rescale_kernel(const float* __restrict__ 
         const float4 a = *reinterpret_cast<const float4*>(ws + t * Co + o);
         const float4 s = *reinterpret_cast<const float4*>(dw + o);
         const float st = dx[t];
-        uint16_t* dst = out + t * ldo + o;
-        dst[0] = f32_to_bf16_rne((a.x * st) * s.x);
-        dst[1] = f32_to_bf16_rne((a.y * st) * s.y);
-        dst[2] = f32_to_bf16_rne((a.z * st) * s.z);
-        dst[3] = f32_to_bf16_rne((a.w * st) * s.w);
+        uint2 packed;
+        packed.x = (uint32_t)f32_to_bf16_rne((a.x * st) * s.x) |
+                   ((uint32_t)f32_to_bf16_rne((a.y * st) * s.y) << 16);
+        packed.y = (uint32_t)f32_to_bf16_rne((a.z * st) * s.z) |
+                   ((uint32_t)f32_to_bf16_rne((a.w * st) * s.w) << 16);
+        *reinterpret_cast<uint2*>(out + t * ldo + o) = packed;
     }
 }
 
