@@ -86,9 +86,13 @@ size_t ptpc_weight_packed_bytes(int64_t Ci, int64_t Co);
  * pre-quantized checkpoint -- §TL;DR / §Getting started).
  *   w         [Ci x Co] bf16, pitch ldw (>= Co)             -- read
  *   w_packed  ptpc_weight_packed_bytes(Ci, Co) bytes         -- written
- *             layout: E4M3 code of w[k][o] at byte o*Kp + k with
- *             Kp = roundup(Ci, 128), zero codes for Ci <= k < Kp
- *             (the K-contiguous order the GEMM's MFMA B operand reads).
+ *             layout (opaque to callers; ptpc_unpack_weight inverts it):
+ *             Kp = roundup(Ci, 128); 1 KB blocks, block (g, s) for
+ *             g < Co/16, s < Kp/64 at byte (g*Kp/64 + s)*1024; the 16-byte
+ *             unit u of a block holds the codes of w[64s+16c .. 64s+16c+15]
+ *             [16g + u/4] with c = (u%4) ^ ((u/16)%4); codes for k >= Ci are
+ *             zero.  This is the GEMM's LDS order for its MFMA B operand, so
+ *             the GEMM streams the weight as contiguous 1 KB reads.
  *   dw        [Co] fp32, dw[o] = max_k |w[k,o]| / 448 (1 for a zero column);
  *             also used as the column-amax scratch during the call.
  */

@@ -10,11 +10,14 @@
 // acc[t,o] = sum_k qx[t,k] * qw[k,o] on OCP E4M3 values, fp32 accumulation
 // in v_mfma_f32_32x32x64_f8f6f4.
 //
-// Data layout: qx is [T x Ci] row-major (K contiguous); the packed weight is
-// [Co x Kp] (K contiguous, Kp = roundup(Ci, 128), zero codes past Ci), so A
-// and B tiles are both "rows of 128 K bytes" and both MFMA operands are read
-// from LDS the same way: lane l takes row l % 32 of a 32-row slab and 32
-// consecutive K bytes starting at 32 * (l / 32) within a 64-byte K step.
+// Data layout: qx is [T x Ci] row-major (K contiguous).  The packed weight
+// is a sequence of 1 KB blocks, [Co/16][Kp/64] of them (Kp = roundup(Ci,
+// 128), zero codes past Ci): block (g, s) holds columns 16g..16g+15 for K
+// bytes 64s..64s+63, laid out exactly as one load instruction drops it into
+// LDS (16 rows of 64 bytes, chunks in swizzled slots), so B tiles stream as
+// contiguous 1 KB reads.  In LDS both operands are "rows of 64 K bytes" and
+// both MFMA operands are read the same way: lane l takes row l % 32 of a
+// 32-row slab and 32 consecutive K bytes starting at 32 * (l / 32).
 //
 // Pipeline: tiles move HBM/L2 -> LDS with buffer_load_dwordx4 ... lds (no
 // staging registers, no ds_write); the buffer descriptor's range check
@@ -30,8 +33,11 @@
 
 namespace ptpc {
 
+#ifndef PTPC_NSTAGE
+#define PTPC_NSTAGE 4
+#endif
+
 constexpr int BK = 64;          // K bytes per pipeline stage (one MFMA K step)
-constexpr int NSTAGE = 4;       // LDS ring depth
 constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
@@ -62,7 +68,7 @@ __device__ __forceinline__ void wait_counts() {
     __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
 }
 
-template <int BM, int BN, int WM, int WN, bool FUSED>
+template <int BM, int BN, int WM, int WN, int NSTAGE, bool FUSED>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
     const uint8_t* __restrict__ wp, int64_t Kp, const float* __restrict__ dw,
@@ -81,10 +87,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     // Distinct LDS objects per stage (not one array indexed by stage) so
     // that the compiler can tell the stage being filled from the stage being
     // read and does not wait for the fills before the reads.
+    static_assert(NSTAGE >= 2 && NSTAGE <= 5, "ring depth");
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage2[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage3[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage2[NSTAGE > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage3[NSTAGE > 3 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage4[NSTAGE > 4 ? STAGE : 16];
+    uint8_t* const stages[5] = {stage0, stage1, stage2, stage3, stage4};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -114,11 +123,14 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
         a_chunk[p] = c;
         a_off[p] = (r < a_rows) ? (uint32_t)(r * ldq + c * 16) : kOutOfRange;
     }
+    // The packed weight is already in LDS order: 1 KB blocks of 16 columns x
+    // one 64-byte K step, lane L's 16 bytes at L*16 (see the packing kernel).
+    const int kblocks = (int)(Kp / BK);
 #pragma unroll
     for (int p = 0; p < B_PER_W; ++p) {
-        const int r = (wave + p * NW) * ROWS_PER_BLK + lrow;
-        const int c = slot ^ swz(r);
-        b_off[p] = (r < b_rows) ? (uint32_t)(r * Kp + c * 16) : kOutOfRange;
+        const int blk = wave + p * NW;                      // 16-column group in the tile
+        b_off[p] = (blk * ROWS_PER_BLK < b_rows) ? (uint32_t)(blk * kblocks * 1024 + lane * 16)
+                                                 : kOutOfRange;
     }
 
     auto issue_stage = [&](int ks, uint8_t* sa) {
@@ -134,7 +146,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
         const bool kin_b = k0 < Kp;
 #pragma unroll
         for (int p = 0; p < B_PER_W; ++p) {
-            const uint32_t off = (b_off[p] != kOutOfRange && kin_b) ? b_off[p] + k0 : kOutOfRange;
+            const uint32_t off =
+                (b_off[p] != kOutOfRange && kin_b) ? b_off[p] + (uint32_t)ks * 1024u : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rb, (lds_ptr_t)(sb + (wave + p * NW) * 1024), 16, off, 0, 0, 0);
         }
@@ -208,36 +221,34 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    // Top of K step s: the stage s+1 fill has landed (two later stages may
-    // still be in flight) and every wave has read stage s into registers, so
-    // stage s%4 is free for the fill of step s+4 (issued inside step s).
+    // Top of K step s: the stage s+1 fill has landed (the fills of the
+    // NSTAGE-2 later steps may still be in flight) and every wave has read
+    // stage s into registers, so stage s%NSTAGE is free for the fill of step
+    // s+NSTAGE (issued inside step s).
     auto top = [&]() {
-        wait_counts<2 * DPW, 0>();
+        wait_counts<(NSTAGE - 2) * DPW, 0>();
         lds_barrier();
     };
 
-    // Ring of four stages; K steps past the data are filled with zeros (all
-    // offsets out of range) so the loop needs no branch; at most three extra
-    // zero steps are multiplied.  The loop is unrolled by four so every
-    // access names its stage.
-    v8i fa0[MT], fb0[NTL], fa1[MT], fb1[NTL];
+    // Ring of NSTAGE stages; K steps past the data are filled with zeros
+    // (every offset out of range) so the loop needs no branch; fewer than
+    // U extra zero steps are multiplied.  The loop is unrolled so that every
+    // access names its stage and fragment set statically.
+    constexpr int U = (NSTAGE % 2) ? 2 * NSTAGE : NSTAGE;
+    v8i fr_a[2][MT], fr_b[2][NTL];
     if (nks > 0) {
-        issue_stage(0, stage0);
-        issue_stage(1, stage1);
-        issue_stage(2, stage2);
-        issue_stage(3, stage3);
-        wait_counts<3 * DPW, 15>();     // stage 0 landed
+#pragma unroll
+        for (int u = 0; u < NSTAGE; ++u) issue_stage(u, stages[u]);
+        wait_counts<(NSTAGE - 1) * DPW, 15>();   // stage 0 landed
         lds_barrier();
-        read_frags(stage0, fa0, fb0);
-        for (int s = 0; s < nks; s += NSTAGE) {
-            top();
-            step(s, fa0, fb0, stage1, fa1, fb1, stage0);
-            top();
-            step(s + 1, fa1, fb1, stage2, fa0, fb0, stage1);
-            top();
-            step(s + 2, fa0, fb0, stage3, fa1, fb1, stage2);
-            top();
-            step(s + 3, fa1, fb1, stage0, fa0, fb0, stage3);
+        read_frags(stage0, fr_a[0], fr_b[0]);
+        for (int s = 0; s < nks; s += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                top();
+                step(s + u, fr_a[u & 1], fr_b[u & 1], stages[(u + 1) % NSTAGE],
+                     fr_a[(u + 1) & 1], fr_b[(u + 1) & 1], stages[u % NSTAGE]);
+            }
         }
         wait_counts<0, 0>();            // no fill may land after the loop
         lds_barrier();
@@ -297,17 +308,17 @@ __global__ __launch_bounds__(256) void rescale_kernel(const float* __restrict__ 
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NS>
 static hipError_t launch_tiles(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                                const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                                int64_t ldo, float* fp32_out, hipStream_t s) {
     const dim3 grid((unsigned)((Co + BN - 1) / BN), (unsigned)((T + BM - 1) / BM));
     const int64_t Kp = round_up_k(Ci);
     if (fp32_out == nullptr) {
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, true>), grid, dim3(WM * WN * 64), 0, s,
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, true>), grid, dim3(WM * WN * 64), 0, s,
                            qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out, ldo);
     } else {
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, false>), grid, dim3(WM * WN * 64), 0, s,
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, false>), grid, dim3(WM * WN * 64), 0, s,
                            qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)fp32_out, Co);
     }
     return hipGetLastError();
@@ -318,11 +329,11 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
                        int64_t ldo, float* fp32_out, hipStream_t s) {
     hipError_t e;
     if (T >= 512 && Co >= 2048)
-        e = launch_tiles<256, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_tiles<256, 256, 2, 2, PTPC_NSTAGE>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
     else if (T > 32)
-        e = launch_tiles<128, 128, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
     else
-        e = launch_tiles<32, 64, 1, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_tiles<32, 64, 1, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
     if (e != hipSuccess || fp32_out == nullptr) return e;
     const int64_t n = T * (Co / 4);
     int64_t blocks = (n + 255) / 256;

@@ -220,10 +220,16 @@ __global__ void weight_scale_kernel(float* __restrict__ dw, int64_t Co) {
     if (o < Co) dw[o] = scale_from_amax(dw[o]);
 }
 
+// Packed weight layout (what the GEMM streams): 1 KB blocks of 16 columns x
+// 64 K bytes, block (g, s) at byte ((g * Kp/64) + s) * 1024.  Inside a block
+// the 16-byte unit u holds column 16g + u/4, K bytes 64s + 16c .. +15 with
+// c = (u % 4) ^ ((u / 16) % 4): the GEMM's LDS row order with its bank
+// swizzle already applied, so one load instruction copies a block verbatim.
+__device__ __forceinline__ int pack_chunk_of_unit(int u) { return (u & 3) ^ ((u >> 4) & 3); }
+
 // Tile: 128 rows of K x 64 columns.  Each thread loads 16 bytes (8 columns)
 // of one row per pass, quantizes them with its 8 column divisors and drops
-// the codes transposed into LDS; the tile then leaves as 64 packed rows of
-// 128 contiguous K bytes.
+// the codes transposed into LDS; the tile then leaves as 8 packed blocks.
 constexpr int kPackK = 128;
 constexpr int kPackN = 64;
 constexpr int kPackPitch = kPackK + 16;   // keeps 16-byte alignment of rows
@@ -260,15 +266,19 @@ __global__ __launch_bounds__(256) void weight_pack_kernel(
         }
     }
     __syncthreads();
-    // 64 columns x 128 bytes = 512 vectors of 16 bytes: two per thread.
+    // 4 column groups x 2 K steps = 8 blocks = 512 units of 16 bytes.
+    const int64_t kblocks = Kp / 64;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const int i = p * 256 + tid;
-        const int n = i >> 3;
-        const int c = i & 7;
+        const int b = i >> 6, u = i & 63;
+        const int g = b >> 1, ks = b & 1;
+        const int n = g * 16 + (u >> 2);
         if (o0 + n < Co) {
-            uint4 val = *reinterpret_cast<const uint4*>(tile + n * kPackPitch + c * 16);
-            *reinterpret_cast<uint4*>(packed + (o0 + n) * Kp + k0 + c * 16) = val;
+            const uint4 val = *reinterpret_cast<const uint4*>(
+                tile + n * kPackPitch + ks * 64 + pack_chunk_of_unit(u) * 16);
+            const int64_t blk = ((o0 >> 4) + g) * kblocks + (k0 >> 6) + ks;
+            *reinterpret_cast<uint4*>(packed + blk * 1024 + u * 16) = val;
         }
     }
 }
@@ -305,10 +315,14 @@ hipError_t launch_quant_weight(const uint16_t* w, int64_t Ci, int64_t Co, int64_
 __global__ void unpack_kernel(const uint8_t* __restrict__ packed, int64_t Ci, int64_t Co,
                               int64_t Kp, uint8_t* __restrict__ qw) {
     const int64_t n = Ci * Co;
+    const int64_t kblocks = Kp / 64;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t k = i / Co, o = i - k * Co;
-        qw[i] = packed[o * Kp + k];
+        const int row = (int)(o & 15), chunk = (int)((k & 63) >> 4);
+        const int u = row * 4 + (chunk ^ ((row >> 2) & 3));    // inverse of the packing
+        const int64_t blk = (o >> 4) * kblocks + (k >> 6);
+        qw[i] = packed[blk * 1024 + u * 16 + (k & 15)];
     }
 }
 

@@ -53,3 +53,18 @@ def sample_indices(T, Co, n, seed):
 def oracle_sampled_ref(qx, dx, qw, dw, rows, cols):
     acc = oracle.gemm_exact_sampled(qx, qw, rows, cols)
     return oracle.apply_scales_sampled(acc, rows, cols, dx, dw)
+
+
+def packed_byte_index(Ci, Co):
+    """Byte offset in the packed weight of the code of w[k][o], for every
+    (k, o) with k < Kp, from the layout include/ptpc.h documents:
+    block (g, s) = (o // 16, k // 64) at (g * Kp/64 + s) * 1024; unit
+    u = 4 * (o % 16) + (c ^ ((o % 16) // 4 % 4)) with c = (k % 64) // 16;
+    byte k % 16 of the unit.  Returns an int64 array [Kp, Co]."""
+    Kp = (Ci + 127) // 128 * 128
+    k = np.arange(Kp, dtype=np.int64)[:, None]
+    o = np.arange(Co, dtype=np.int64)[None, :]
+    row = o % 16
+    c = (k % 64) // 16
+    u = 4 * row + (c ^ ((row // 4) % 4))
+    return ((o // 16) * (Kp // 64) + k // 64) * 1024 + u * 16 + k % 16

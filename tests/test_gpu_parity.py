@@ -16,7 +16,7 @@ import torch
 import oracle
 import workloads
 from gpu_helpers import (bits_to_dev, check_close, dev_to_bits, oracle_sampled_ref,
-                         sample_indices)
+                         packed_byte_index, sample_indices)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,9 +64,13 @@ def check_quant(g, x_bits, w_bits, what):
     bad = np.argwhere(g["qw"] != qw)
     assert bad.size == 0, f"{what}: {len(bad)} weight codes differ, first {bad[:5].tolist()}"
     Ci, Co = w_bits.shape
-    Kp = (Ci + 127) // 128 * 128
-    packed = g["packed"].reshape(Co, Kp)
-    assert np.all(packed[:, Ci:] == 0), f"{what}: K padding not zero"
+    if Ci * Co <= (1 << 26):
+        # the documented packed layout, read directly (not via unpack_weight)
+        idx = packed_byte_index(Ci, Co)
+        packed = g["packed"]
+        assert packed.size == idx.size, f"{what}: packed size"
+        assert np.array_equal(packed[idx[:Ci]], qw), f"{what}: packed layout"
+        assert np.all(packed[idx[Ci:]] == 0), f"{what}: K padding not zero"
     return qx, dx, qw, dw
 
 
