@@ -209,7 +209,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
 #pragma unroll
             for (int j = 0; j < NTL; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+                    b[j], a[i], acc[i][j], 0, 0, 0, 0, 0, 0);
         read_frags(nxt, na, nb);
         issue_stage(s + NSTAGE, refill);
         constexpr int NQ = NMFMA > NREAD ? NMFMA : NREAD;
@@ -254,30 +254,36 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
         lds_barrier();
     }
 
-    // Epilogue.  Accumulator element e of a 32x32 tile in lane l sits at
-    // row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+    // Epilogue.  The weight slab is the MFMA's first operand, so the 32x32
+    // accumulator tile is out^T: in lane l, element e holds output row
+    // (token) l%32 of the slab and output column 8*(e/4) + 4*(l/32) + e%4.
+    // Each lane therefore owns runs of 4 consecutive columns of one row:
+    // 8-byte bf16 stores (16-byte fp32 stores in the two-step form).
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-        float sx[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
-            sx[e] = (FUSED && row < T) ? dx[row] : 0.0f;
-        }
+        const int64_t row = m0 + wm * WTM + i * 32 + lr;
+        if (row >= T) continue;
+        const float sx = FUSED ? dx[row] : 0.0f;
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
-            const int64_t col = n0 + wn * WTN + j * 32 + lr;
-            if (col >= Co) continue;
-            const float sw = FUSED ? dw[col] : 0.0f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
-                if (row >= T) continue;
+            for (int g = 0; g < 4; ++g) {
+                const int64_t col = n0 + wn * WTN + j * 32 + 8 * g + 4 * lg;
+                if (col >= Co) continue;                  // Co % 16 == 0: runs are whole
+                const float a0 = acc[i][j][4 * g + 0], a1 = acc[i][j][4 * g + 1];
+                const float a2 = acc[i][j][4 * g + 2], a3 = acc[i][j][4 * g + 3];
                 if constexpr (FUSED) {
-                    const float v = (acc[i][j][e] * sx[e]) * sw;
-                    reinterpret_cast<uint16_t*>(out)[row * ldo + col] = f32_to_bf16_rne(v);
+                    const float4 sw = *reinterpret_cast<const float4*>(dw + col);
+                    uint2 pk;
+                    pk.x = (uint32_t)f32_to_bf16_rne((a0 * sx) * sw.x) |
+                           ((uint32_t)f32_to_bf16_rne((a1 * sx) * sw.y) << 16);
+                    pk.y = (uint32_t)f32_to_bf16_rne((a2 * sx) * sw.z) |
+                           ((uint32_t)f32_to_bf16_rne((a3 * sx) * sw.w) << 16);
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + row * ldo + col) =
+                        pk;
                 } else {
-                    reinterpret_cast<float*>(out)[row * Co + col] = acc[i][j][e];
+                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * Co + col) =
+                        make_float4(a0, a1, a2, a3);
                 }
             }
         }
