@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="run a plain device copy of this many MiB (3x) before timing, "
                         "as the reference kernel for HBM byte counters")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
+                        "--only gemm_fused --copy-calibration-mb run into the traffic record "
+                        "and exit (no GPU needed)")
     return p.parse_args()
 
 
@@ -65,6 +69,41 @@ def measured_traffic(workload):
     if t.get("workload") != workload or t.get("gemm_source_sha256_16") != gemm_source_hash():
         return None
     return t.get("bytes_per_launch")
+
+
+def traffic_record(fetch_csv, write_csv, workload, copy_mb):
+    """HBM bytes per fused-GEMM launch: the FETCH_SIZE / WRITE_SIZE counters
+    (KiB per dispatch) of the GEMM, each scaled by the ratio of the known
+    bytes of a plain device copy to what the same counter reads for it."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"]
+                key = ("gemm" if "gemm_kernel" in name and "true>" in name
+                       else "copy" if "copyBuffer" in name else None)
+                if key:
+                    vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in vals.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = float(copy_mb) * (1 << 20)
+    f_factor = copy_bytes / (f["copy"] * 1024.0)
+    w_factor = copy_bytes / (w["copy"] * 1024.0)
+    fetch = f["gemm"] * 1024.0 * f_factor
+    write = w["gemm"] * 1024.0 * w_factor
+    return {"workload": workload, "gemm_source_sha256_16": gemm_source_hash(),
+            "kernel": "gemm_kernel<..., true> (fused)",
+            "fetch_kib_raw": f["gemm"], "write_kib_raw": w["gemm"],
+            "copy_bytes": copy_bytes, "copy_fetch_kib_raw": f["copy"],
+            "copy_write_kib_raw": w["copy"], "fetch_factor": f_factor,
+            "write_factor": w_factor, "fetch_bytes": fetch, "write_bytes": write,
+            "bytes_per_launch": fetch + write}
 
 
 def cpu_baseline(x_bits, w_bits, target_s):
@@ -104,6 +143,11 @@ def cpu_baseline(x_bits, w_bits, target_s):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        rec = traffic_record(args.traffic_from[0], args.traffic_from[1], args.workload,
+                             args.copy_calibration_mb or 1024)
+        print(json.dumps(rec, indent=1))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}), flush=True)
