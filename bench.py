@@ -33,7 +33,8 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=30,
+                   help="untimed steps first; the shader clock needs tens of ms to settle")
     p.add_argument("--workload", default="70b_down")
     p.add_argument("--layer", default=None, help="70b_sweep layer")
     p.add_argument("--T", type=int, default=None)

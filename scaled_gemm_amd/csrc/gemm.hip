@@ -28,24 +28,25 @@
 // over the banks.  A load instruction fills 1 KB of LDS (64 lanes x 16 B,
 // i.e. 8 rows), so each lane fetches the global chunk that belongs in its
 // fixed LDS slot.
+#include <utility>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace ptpc {
 
-#ifndef PTPC_NSTAGE
-#define PTPC_NSTAGE 4
-#endif
-
-constexpr int BK = 64;          // K bytes per pipeline stage (one MFMA K step)
+constexpr int BK = 64;          // K bytes per step (one MFMA K step)
 constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// Chunk slot of logical 16-byte chunk c in LDS row r.  A row is 64 bytes
-// (4 chunks); an operand read has 16 consecutive rows of one logical chunk in
-// flight per LDS cycle on the 64-bank LDS, and rows r, r+4, r+8, r+12 share
-// banks unless their slots differ.
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+// LDS bank swizzles (64 banks of 4 bytes; an operand read has 16 consecutive
+// rows of one logical 16-byte chunk in flight per LDS cycle).
+//   B rows are 64 bytes (4 chunks): rows r, r+4, r+8, r+12 share banks
+//   unless their slots differ -> slot = c ^ ((r >> 2) & 3).
+//   A rows are 128 bytes (8 chunks, two K steps): rows r and r+2 share
+//   banks unless their slots differ -> slot = c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int swz_b(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 7; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -68,7 +69,23 @@ __device__ __forceinline__ void wait_counts() {
     __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
 }
 
-template <int BM, int BN, int WM, int WN, int NSTAGE, bool FUSED>
+constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
+
+// The pipeline.  K advances in 64-byte steps; each step is one MFMA K
+// step for every accumulator tile.
+//   A (token rows of qx, row-major in HBM) is staged in "pair slots": one
+//   slot holds two consecutive K steps as 128-byte LDS rows, so every A load
+//   fetches whole 128-byte lines.  Three pair slots.
+//   B (the packed weight) is staged one step per slot, NB slots of 64-byte
+//   rows, filled by verbatim 1 KB block copies.
+// Each step issues the same number of loads: the B fill for step s+NB and
+// half (by rows) of the A pair that is two pairs ahead: at an even step s the
+// second half of pair (s+4, s+5), at an odd step s the first half of pair
+// (s+5, s+6).  At the top of step t the fills read during step t (operands
+// of step t+1) were issued at the top of step t-2 or earlier (t+1-NB or
+// earlier for B), so with uniform issue counts one "vmcnt <= loads issued
+// in the last NB-2 steps" wait covers both.
+template <int BM, int BN, int WM, int WN, int NB, bool FUSED>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
     const uint8_t* __restrict__ wp, int64_t Kp, const float* __restrict__ dw,
@@ -76,24 +93,28 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MT = WTM / 32, NTL = WTN / 32;
-    constexpr int ROWS_PER_BLK = 1024 / BK;                   // rows one load instruction fills
-    constexpr int A_BLK = BM / ROWS_PER_BLK, B_BLK = BN / ROWS_PER_BLK;
-    constexpr int A_PER_W = A_BLK / NW, B_PER_W = B_BLK / NW;
-    constexpr int DPW = A_PER_W + B_PER_W;                    // load instructions per wave per stage
-    static_assert(A_PER_W * NW == A_BLK && B_PER_W * NW == B_BLK, "tile/waves mismatch");
-    static_assert(2 * DPW < 64, "vmcnt range");
-    constexpr int A_BYTES = BM * BK;
-    constexpr int STAGE = (BM + BN) * BK;
-    // Distinct LDS objects per stage (not one array indexed by stage) so
-    // that the compiler can tell the stage being filled from the stage being
-    // read and does not wait for the fills before the reads.
-    static_assert(NSTAGE >= 2 && NSTAGE <= 5, "ring depth");
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage2[NSTAGE > 2 ? STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage3[NSTAGE > 3 ? STAGE : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage4[NSTAGE > 4 ? STAGE : 16];
-    uint8_t* const stages[5] = {stage0, stage1, stage2, stage3, stage4};
+    constexpr int A_BLK = BM / 8;                    // A pair: 8 rows x 128 B per load
+    constexpr int B_BLK = BN / 16;                   // B step: 16 rows x 64 B per load
+    constexpr int A_HALF_PER_W = A_BLK / 2 / NW;     // loads per wave per half pair
+    constexpr int B_PER_W = B_BLK / NW;
+    constexpr int DPW = A_HALF_PER_W + B_PER_W;      // loads per wave per step
+    static_assert(A_HALF_PER_W * 2 * NW == A_BLK && B_PER_W * NW == B_BLK, "tile/waves");
+    static_assert(NB == 3 || NB == 4, "B ring depth");
+    static_assert((NB - 2) * DPW < 64, "vmcnt range");
+    constexpr int A_SLOT = BM * 2 * BK;              // one pair slot
+    constexpr int B_SLOT = BN * BK;
+    // Distinct LDS objects per slot (not one array indexed by slot) so that
+    // the compiler can tell the slot being filled from the slot being read
+    // and does not wait for fills before reads.
+    __shared__ __attribute__((aligned(1024))) uint8_t a_s0[A_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t a_s1[A_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t a_s2[A_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t b_s0[B_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t b_s1[B_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t b_s2[B_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t b_s3[NB > 3 ? B_SLOT : 16];
+    uint8_t* const a_slots[3] = {a_s0, a_s1, a_s2};
+    uint8_t* const b_slots[4] = {b_s0, b_s1, b_s2, b_s3};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -101,7 +122,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     const int wm = wave / WN, wn = wave % WN;
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int nks = (int)(Kp / BK);                           // K steps with data
+    const int nks = (int)(Kp / BK);                  // K steps with data (even)
 
     // Buffer descriptors based at this tile's first row; rows past the end
     // and K past the data land beyond num_records and read as zero.
@@ -110,46 +131,51 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(qx + m0 * ldq, (uint32_t)(a_rows * ldq));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(wp + n0 * Kp, (uint32_t)(b_rows * Kp));
 
-    // A load instruction fills ROWS_PER_BLK rows: lane L owns LDS row L/4,
-    // slot L%4, and fetches the logical chunk that belongs in that slot.
-    const int lrow = lane >> 2;
-    const int slot = lane & 3;
-    uint32_t a_off[A_PER_W], b_off[B_PER_W];
-    int a_chunk[A_PER_W];
+    // A pair load: lane L owns LDS row L/8 of its 8-row block, slot L%8, and
+    // fetches the logical chunk that belongs in that slot.
+    uint32_t a_off[2][A_HALF_PER_W];
+    int a_chunk[2][A_HALF_PER_W];
 #pragma unroll
-    for (int p = 0; p < A_PER_W; ++p) {
-        const int r = (wave + p * NW) * ROWS_PER_BLK + lrow;
-        const int c = slot ^ swz(r);
-        a_chunk[p] = c;
-        a_off[p] = (r < a_rows) ? (uint32_t)(r * ldq + c * 16) : kOutOfRange;
-    }
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int p = 0; p < A_HALF_PER_W; ++p) {
+            const int blk = h * (A_BLK / 2) + wave + p * NW;
+            const int r = blk * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swz_a(r);
+            a_chunk[h][p] = c;
+            a_off[h][p] = (r < a_rows) ? (uint32_t)(r * ldq + c * 16) : kOutOfRange;
+        }
     // The packed weight is already in LDS order: 1 KB blocks of 16 columns x
     // one 64-byte K step, lane L's 16 bytes at L*16 (see the packing kernel).
-    const int kblocks = (int)(Kp / BK);
+    uint32_t b_off[B_PER_W];
 #pragma unroll
     for (int p = 0; p < B_PER_W; ++p) {
-        const int blk = wave + p * NW;                      // 16-column group in the tile
-        b_off[p] = (blk * ROWS_PER_BLK < b_rows) ? (uint32_t)(blk * kblocks * 1024 + lane * 16)
-                                                 : kOutOfRange;
+        const int blk = wave + p * NW;               // 16-column group in the tile
+        b_off[p] = (blk * 16 < b_rows) ? (uint32_t)(blk * nks * 1024 + lane * 16) : kOutOfRange;
     }
 
-    auto issue_stage = [&](int ks, uint8_t* sa) {
-        const int k0 = ks * BK;
-        uint8_t* sb = sa + A_BYTES;
+    // Loads of one half (h) of the A pair holding steps 2q, 2q+1.
+    auto issue_a_half = [&](int q, int h, uint8_t* slot) {
+        const int k0 = q * 2 * BK;
 #pragma unroll
-        for (int p = 0; p < A_PER_W; ++p) {
-            const bool kin = (int64_t)(k0 + a_chunk[p] * 16) < Ci;
-            const uint32_t off = (a_off[p] != kOutOfRange && kin) ? a_off[p] + k0 : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_ptr_t)(sa + (wave + p * NW) * 1024), 16, off, 0, 0, 0);
+        for (int p = 0; p < A_HALF_PER_W; ++p) {
+            const bool kin = (int64_t)(k0 + a_chunk[h][p] * 16) < Ci;
+            const uint32_t off = (a_off[h][p] != kOutOfRange && kin) ? a_off[h][p] + k0
+                                                                     : kOutOfRange;
+            const int blk = h * (A_BLK / 2) + wave + p * NW;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + blk * 1024), 16, off,
+                                                     0, 0, 0);
         }
-        const bool kin_b = k0 < Kp;
+    };
+    // Loads of B for step ks.
+    auto issue_b = [&](int ks, uint8_t* slot) {
+        const bool kin = ks < nks;
 #pragma unroll
         for (int p = 0; p < B_PER_W; ++p) {
             const uint32_t off =
-                (b_off[p] != kOutOfRange && kin_b) ? b_off[p] + (uint32_t)ks * 1024u : kOutOfRange;
+                (b_off[p] != kOutOfRange && kin) ? b_off[p] + (uint32_t)ks * 1024u : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_ptr_t)(sb + (wave + p * NW) * 1024), 16, off, 0, 0, 0);
+                rb, (lds_ptr_t)(slot + (wave + p * NW) * 1024), 16, off, 0, 0, 0);
         }
     };
 
@@ -163,55 +189,68 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
 
     const int lr = lane & 31;
     const int lg = lane >> 5;
-    // MFMA operands: lane l reads row l%32 of a 32-row slab, logical chunks
-    // 2*(l/32) and 2*(l/32)+1 of the 64-byte K step.
-    int a_lo[MT], a_hi[MT], b_lo[NTL], b_hi[NTL];
+    // MFMA operands: lane l reads row l%32 of a 32-row slab and logical
+    // chunks 2*(l/32), 2*(l/32)+1 of the 64-byte K step (for A, of the step's
+    // half of the 128-byte pair row).
+    int a_row[MT], a_sw[MT], b_lo[NTL], b_hi[NTL];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
         const int r = wm * WTM + i * 32 + lr;
-        a_lo[i] = r * BK + (((2 * lg) ^ swz(r)) << 4);
-        a_hi[i] = r * BK + (((2 * lg + 1) ^ swz(r)) << 4);
+        a_row[i] = r * 2 * BK;
+        a_sw[i] = swz_a(r);
     }
 #pragma unroll
     for (int j = 0; j < NTL; ++j) {
         const int r = wn * WTN + j * 32 + lr;
-        b_lo[j] = A_BYTES + r * BK + (((2 * lg) ^ swz(r)) << 4);
-        b_hi[j] = A_BYTES + r * BK + (((2 * lg + 1) ^ swz(r)) << 4);
+        b_lo[j] = r * BK + (((2 * lg) ^ swz_b(r)) << 4);
+        b_hi[j] = r * BK + (((2 * lg + 1) ^ swz_b(r)) << 4);
     }
-    auto read_frags = [&](const uint8_t* st, v8i (&a)[MT], v8i (&b)[NTL]) {
+    auto read_frags = [&](const uint8_t* as, int half, const uint8_t* bs, v8i (&a)[MT],
+                          v8i (&b)[NTL]) {
+        const int c0 = half * 4 + 2 * lg;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-            const uint4 lo = *reinterpret_cast<const uint4*>(st + a_lo[i]);
-            const uint4 hi = *reinterpret_cast<const uint4*>(st + a_hi[i]);
+            const uint4 lo = *reinterpret_cast<const uint4*>(as + a_row[i] + ((c0 ^ a_sw[i]) << 4));
+            const uint4 hi =
+                *reinterpret_cast<const uint4*>(as + a_row[i] + (((c0 + 1) ^ a_sw[i]) << 4));
             a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
-            const uint4 lo = *reinterpret_cast<const uint4*>(st + b_lo[j]);
-            const uint4 hi = *reinterpret_cast<const uint4*>(st + b_hi[j]);
+            const uint4 lo = *reinterpret_cast<const uint4*>(bs + b_lo[j]);
+            const uint4 hi = *reinterpret_cast<const uint4*>(bs + b_hi[j]);
             b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
     };
-    // One K step: its MFMAs, with the next step's operand reads and the
-    // loads that refill the just-freed stage threaded between them (the
-    // reads fill the other fragment registers).  Issuing the loads in one
-    // burst would hold back the first MFMA until the texture unit accepted
-    // them all.
+
+    // Step s: its MFMAs, with the operand reads of step s+1 and the step's
+    // loads threaded between them (the reads fill the other fragment
+    // registers; issuing the loads in one burst would hold back the MFMAs).
     constexpr int NMFMA = MT * NTL;
     constexpr int NREAD = 2 * (MT + NTL);
-    auto step = [&](int s, const v8i (&a)[MT], const v8i (&b)[NTL], const uint8_t* nxt,
-                    v8i (&na)[MT], v8i (&nb)[NTL], uint8_t* refill) {
+    v8i fr_a[2][MT], fr_b[2][NTL];
+    auto step = [&](auto U, int s) {
+        constexpr int u = decltype(U)::value;        // s % period, static
+        // operands of step s+1
+        constexpr int n = u + 1;
+        const uint8_t* na = a_slots[(n / 2) % 3];
+        const uint8_t* nb = b_slots[n % NB];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
             for (int j = 0; j < NTL; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    b[j], a[i], acc[i][j], 0, 0, 0, 0, 0, 0);
-        read_frags(nxt, na, nb);
-        issue_stage(s + NSTAGE, refill);
+                    fr_b[u & 1][j], fr_a[u & 1][i], acc[i][j], 0, 0, 0, 0, 0, 0);
+        read_frags(na, n & 1, nb, fr_a[n & 1], fr_b[n & 1]);
+        issue_b(s + NB, b_slots[u % NB]);
+        if constexpr ((u & 1) == 0) {
+            issue_a_half((s + 4) / 2, 1, a_slots[((u + 4) / 2) % 3]);
+        } else {
+            issue_a_half((s + 5) / 2, 0, a_slots[((u + 5) / 2) % 3]);
+        }
         constexpr int NQ = NMFMA > NREAD ? NMFMA : NREAD;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
@@ -221,34 +260,32 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    // Top of K step s: the stage s+1 fill has landed (the fills of the
-    // NSTAGE-2 later steps may still be in flight) and every wave has read
-    // stage s into registers, so stage s%NSTAGE is free for the fill of step
-    // s+NSTAGE (issued inside step s).
     auto top = [&]() {
-        wait_counts<(NSTAGE - 2) * DPW, 0>();
+        wait_counts<(NB - 2) * DPW, 0>();
         lds_barrier();
     };
 
-    // Ring of NSTAGE stages; K steps past the data are filled with zeros
-    // (every offset out of range) so the loop needs no branch; fewer than
-    // U extra zero steps are multiplied.  The loop is unrolled so that every
-    // access names its stage and fragment set statically.
-    constexpr int U = (NSTAGE % 2) ? 2 * NSTAGE : NSTAGE;
-    v8i fr_a[2][MT], fr_b[2][NTL];
+    // Steps past the data are zero fills (every offset out of range), so the
+    // loop needs no branch; it runs whole periods of P steps (fewer than P
+    // extra zero steps are multiplied).  Unrolled by the period so that every
+    // slot and fragment set is named statically.
+    constexpr int P = 6 * NB / gcd_c(6, NB);
     if (nks > 0) {
+        // Fills as if issued at the tops of steps -NB .. -1.
+        issue_a_half(0, 0, a_slots[0]);
+        issue_a_half(0, 1, a_slots[0]);
+        issue_a_half(1, 0, a_slots[1]);
+        issue_a_half(1, 1, a_slots[1]);
+        issue_a_half(2, 0, a_slots[2]);
 #pragma unroll
-        for (int u = 0; u < NSTAGE; ++u) issue_stage(u, stages[u]);
-        wait_counts<(NSTAGE - 1) * DPW, 15>();   // stage 0 landed
+        for (int u = 0; u < NB; ++u) issue_b(u, b_slots[u]);
+        wait_counts<0, 0>();
         lds_barrier();
-        read_frags(stage0, fr_a[0], fr_b[0]);
-        for (int s = 0; s < nks; s += U) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                top();
-                step(s + u, fr_a[u & 1], fr_b[u & 1], stages[(u + 1) % NSTAGE],
-                     fr_a[(u + 1) & 1], fr_b[(u + 1) & 1], stages[u % NSTAGE]);
-            }
+        read_frags(a_slots[0], 0, b_slots[0], fr_a[0], fr_b[0]);
+        for (int s0 = 0; s0 < nks; s0 += P) {
+            [&]<int... Us>(std::integer_sequence<int, Us...>) {
+                ((top(), step(std::integral_constant<int, Us>{}, s0 + Us)), ...);
+            }(std::make_integer_sequence<int, P>{});
         }
         wait_counts<0, 0>();            // no fill may land after the loop
         lds_barrier();
@@ -314,17 +351,17 @@ __global__ __launch_bounds__(256) void rescale_kernel(const float* __restrict__ 
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int NB>
 static hipError_t launch_tiles(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                                const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                                int64_t ldo, float* fp32_out, hipStream_t s) {
     const dim3 grid((unsigned)((Co + BN - 1) / BN), (unsigned)((T + BM - 1) / BM));
     const int64_t Kp = round_up_k(Ci);
     if (fp32_out == nullptr) {
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, true>), grid, dim3(WM * WN * 64), 0, s,
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NB, true>), grid, dim3(WM * WN * 64), 0, s,
                            qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out, ldo);
     } else {
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, false>), grid, dim3(WM * WN * 64), 0, s,
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NB, false>), grid, dim3(WM * WN * 64), 0, s,
                            qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)fp32_out, Co);
     }
     return hipGetLastError();
@@ -335,7 +372,7 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
                        int64_t ldo, float* fp32_out, hipStream_t s) {
     hipError_t e;
     if (T >= 512 && Co >= 2048)
-        e = launch_tiles<256, 256, 2, 2, PTPC_NSTAGE>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_tiles<256, 256, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
     else if (T > 32)
         e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
     else
