@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="run a plain device copy of this many MiB (3x) before timing, "
                         "as the reference kernel for HBM byte counters")
+    p.add_argument("--sweep", action="store_true",
+                   help="one JSON line per workload shape (every config, every 70B layer x T): "
+                        "quant_act GB/s, fused / two-step GEMM TFLOP/s; not the bench line")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
                         "--only gemm_fused --copy-calibration-mb run into the traffic record "
@@ -142,8 +145,78 @@ def cpu_baseline(x_bits, w_bits, target_s):
                        f"(weight quantization {t_w:.1f} s); {nthr} OpenMP threads")}
 
 
+def sweep(args):
+    """Per-shape kernel rates over every workload shape (HIP events around each
+    launch on the launch stream, after a warm-up)."""
+    import numpy as np
+    import torch
+
+    import scaled_gemm_amd as sg
+    import workloads
+
+    dev = torch.device("cuda:0")
+    sg.lib()
+    shapes = [("tiny", None, None), ("8b_qkv_decode", None, None), ("8b_gate_up", None, None),
+              ("70b_down", None, None)]
+    shapes += [("70b_sweep", T, layer) for layer in workloads.SWEEP_LAYERS
+               for T in workloads.SWEEP_T]
+    stream = torch.cuda.current_stream()
+    for name, T_, layer in shapes:
+        if name == "70b_sweep":
+            shape, x_bits, w_bits = workloads.make(name, T=T_, layer=layer)
+        else:
+            shape, x_bits, w_bits = workloads.make(name)
+        T, Ci, Co = shape.T, shape.Ci, shape.Co
+        x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        del x_bits, w_bits
+        pw = sg.quant_weight(w)
+        qx, dx = sg.quant_act(x)
+        out = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
+        out2 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((T, Co), dtype=torch.float32, device=dev)
+        calls = {
+            "quant_weight": lambda: sg.quant_weight(w, out=pw),
+            "quant_act": lambda: sg.quant_act(x, qx=qx, dx=dx),
+            "gemm_fused": lambda: sg.gemm(qx, dx, pw, out=out),
+            "gemm_unfused": lambda: sg.gemm_unfused(qx, dx, pw, out=out2, workspace=ws),
+        }
+        ms = {}
+        for k, fn in calls.items():
+            for _ in range(max(3, args.warmup)):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+            for i in range(args.steps):
+                ev[2 * i].record(stream)
+                fn()
+                ev[2 * i + 1].record(stream)
+            torch.cuda.synchronize()
+            ms[k] = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1])
+                                   for i in range(args.steps)]))
+        flops = 2.0 * T * Ci * Co
+        act_b = 3.0 * T * Ci + 4.0 * T
+        print(json.dumps({
+            "workload": shape.name, "T": T, "Ci": Ci, "Co": Co,
+            "ms": {k: round(v, 4) for k, v in ms.items()},
+            "gemm_fused_tflops": round(flops / ms["gemm_fused"] / 1e9, 1),
+            "gemm_fused_frac_fp8_peak": round(flops / ms["gemm_fused"] / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "gemm_fused_gbs_min_bytes": round((T * Ci + Ci * Co + 2.0 * T * Co + 4.0 * (T + Co))
+                                              / ms["gemm_fused"] / 1e6, 1),
+            "gemm_unfused_tflops": round(flops / ms["gemm_unfused"] / 1e9, 1),
+            "fused_over_unfused": round(ms["gemm_unfused"] / ms["gemm_fused"], 3),
+            "quant_act_gbs": round(act_b / ms["quant_act"] / 1e6, 1),
+            "quant_act_frac_hbm": round(act_b / ms["quant_act"] / 1e6 / PEAK_HBM_GBS, 4),
+            "quant_weight_gbs": round((3.0 * Ci * Co + 4.0 * Co) / ms["quant_weight"] / 1e6, 1),
+        }), flush=True)
+        del x, w, pw, qx, dx, out, out2, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
+    if args.sweep:
+        sweep(args)
+        return
     if args.traffic_from:
         rec = traffic_record(args.traffic_from[0], args.traffic_from[1], args.workload,
                              args.copy_calibration_mb or 1024)

@@ -71,6 +71,28 @@ __device__ __forceinline__ void wait_counts() {
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
+// Tile order.  Workgroups are dealt round-robin to the 8 XCDs, each with its
+// own L2.  The linear id is remapped so that XCD x owns a contiguous chunk of
+// the logical order, and the logical order walks groups of kGroupN column
+// blocks, every row block of a group before the next group: a weight block
+// is streamed from HBM once, the activation blocks re-read per group stay in
+// the MALL, and the 32 tiles an XCD holds at once (4 row x 8 column blocks)
+// share 12 operand blocks per K step.
+constexpr int kXcds = 8;
+constexpr int64_t kCus = 256;
+constexpr int kGroupN = 8;
+__device__ __forceinline__ void tile_of(int gm, int gn, int& tm, int& tn) {
+    const int n = gm * gn;
+    int i = blockIdx.x;
+    if (n % kXcds == 0) i = (i % kXcds) * (n / kXcds) + i / kXcds;
+    const int group = i / (kGroupN * gm);
+    const int first_n = group * kGroupN;
+    const int width = (gn - first_n < kGroupN) ? gn - first_n : kGroupN;
+    const int r = i - group * kGroupN * gm;
+    tm = r / width;
+    tn = first_n + r % width;
+}
+
 // The pipeline.  K advances in 64-byte steps; each step is one MFMA K
 // step for every accumulator tile.
 //   A (token rows of qx, row-major in HBM) is staged in "pair slots": one
@@ -120,8 +142,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    int tm, tn;
+    tile_of((int)((T + BM - 1) / BM), (int)((Co + BN - 1) / BN), tm, tn);
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
     const int nks = (int)(Kp / BK);                  // K steps with data (even)
 
     // Buffer descriptors based at this tile's first row; rows past the end
@@ -355,7 +379,7 @@ template <int BM, int BN, int WM, int WN, int NB>
 static hipError_t launch_tiles(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                                const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                                int64_t ldo, float* fp32_out, hipStream_t s) {
-    const dim3 grid((unsigned)((Co + BN - 1) / BN), (unsigned)((T + BM - 1) / BM));
+    const dim3 grid((unsigned)(((Co + BN - 1) / BN) * ((T + BM - 1) / BM)));
     const int64_t Kp = round_up_k(Ci);
     if (fp32_out == nullptr) {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NB, true>), grid, dim3(WM * WN * 64), 0, s,
@@ -370,8 +394,16 @@ static hipError_t launch_tiles(const uint8_t* qx, int64_t ldq, const float* dx, 
 hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                        const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                        int64_t ldo, float* fp32_out, hipStream_t s) {
+    // Tile choice: 256x256 keeps the most MFMA work per loaded byte; when it
+    // leaves CUs idle or a badly filled last round, 256x128 (twice the tiles,
+    // about 10% less efficient per tile) is taken if its rounds cost less.
+    auto rounds = [](int64_t tiles) { return (tiles + kCus - 1) / kCus; };
+    const int64_t t256 = ((T + 255) / 256) * ((Co + 255) / 256);
+    const int64_t t128 = ((T + 255) / 256) * ((Co + 127) / 128);
     hipError_t e;
-    if (T >= 512 && Co >= 2048)
+    if (T >= 256 && 10 * rounds(t128) * 5 < 9 * rounds(t256) * 10)
+        e = launch_tiles<256, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+    else if (T >= 256)
         e = launch_tiles<256, 256, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
     else if (T > 32)
         e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
