@@ -20,6 +20,19 @@ namespace ptpc {
 // 16-byte vectors (8 bf16 each) of the row in registers.  Vector j of thread
 // g is chunk j*G + g, so a group's loads for one j are contiguous.
 // ---------------------------------------------------------------------------
+// Loads of rows held as 8 or more vectors per thread carry the non-temporal
+// hint (X is read once); measured faster there, slower for short rows.
+template <int VPT>
+__device__ __forceinline__ uint4 load_row_vec(const uint4* p) {
+    if constexpr (VPT >= 8) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return make_uint4(t.x, t.y, t.z, t.w);
+    } else {
+        return *p;
+    }
+}
+
 template <int G, int VPT>
 __global__ __launch_bounds__(256) void quant_act_kernel(
     const uint16_t* __restrict__ x, int64_t T, int64_t Ci, int64_t ldx,
@@ -39,7 +52,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
     for (int j = 0; j < VPT; ++j) {
         const int64_t c = (int64_t)j * G + g;
         if (row_ok && c < nchunk) {
-            v[j] = xr[c];
+            v[j] = load_row_vec<VPT>(xr + c);
         } else {
             v[j] = make_uint4(0, 0, 0, 0);
         }
@@ -145,10 +158,14 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t Ci, int64_t ld
         return hipGetLastError();
     }
     const int64_t nchunk = Ci / 8;
-    // Aim for about 8 vectors per thread; groups of 16..256 threads per row.
-    int64_t G = pow2_ceil((nchunk + 7) / 8);
-    if (G < 16) G = 16;
-    if (G > 256) G = 256;
+    // Rows of 256 or more 16-byte vectors get a whole 256-thread workgroup
+    // (more loads in flight per row beat more vectors per thread); shorter
+    // rows share a workgroup, about 8 vectors per thread, at least 16 threads.
+    int64_t G = 256;
+    if (nchunk < 256) {
+        G = pow2_ceil((nchunk + 7) / 8);
+        if (G < 16) G = 16;
+    }
     const int64_t per = (nchunk + G - 1) / G;
     if (per > 16) {
         hipLaunchKernelGGL(quant_act_long_kernel, dim3((unsigned)T), dim3(256), 0, s,
