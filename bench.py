@@ -107,7 +107,20 @@ def traffic_record(fetch_csv, write_csv, workload, copy_mb):
             "copy_bytes": copy_bytes, "copy_fetch_kib_raw": f["copy"],
             "copy_write_kib_raw": w["copy"], "fetch_factor": f_factor,
             "write_factor": w_factor, "fetch_bytes": fetch, "write_bytes": write,
-            "bytes_per_launch": fetch + write}
+            "bytes_per_launch": fetch + write,
+            "commands": [
+                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
+                "-d $REPO/gpurun_out/prof_fetch -o p -- python -u $REPO/bench.py --steps 3 "
+                f"--warmup 1 --no-cpu-baseline --only gemm_fused --copy-calibration-mb {copy_mb}",
+                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv "
+                "-d $REPO/gpurun_out/prof_write -o p -- python -u $REPO/bench.py --steps 3 "
+                f"--warmup 1 --no-cpu-baseline --only gemm_fused --copy-calibration-mb {copy_mb}",
+                "python bench.py --traffic-from $REPO/gpurun_out/prof_fetch/p_counter_collection.csv "
+                f"$REPO/gpurun_out/prof_write/p_counter_collection.csv --copy-calibration-mb {copy_mb}"],
+            "note": ("Counters in KiB per dispatch, averaged over the fused-GEMM launches; each "
+                     "scaled by known copy bytes / counter reading for a device copy of "
+                     f"{copy_mb} MiB (torch copy_) in the same run. On MI355X FETCH_SIZE reads "
+                     "about half of the copy's bytes, WRITE_SIZE all of them.")}
 
 
 def cpu_baseline(x_bits, w_bits, target_s):
@@ -220,6 +233,9 @@ def main():
     if args.traffic_from:
         rec = traffic_record(args.traffic_from[0], args.traffic_from[1], args.workload,
                              args.copy_calibration_mb or 1024)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
         print(json.dumps(rec, indent=1))
         return
     if args.gpus != 1:

@@ -351,6 +351,169 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     }
 }
 
+// Few tokens (T <= 64): the GEMM is a weight stream, bound by HBM.  A
+// workgroup owns NT*32 output columns and all T rows (MT = ceil(T/32) row
+// tiles of 32); its NWAVE waves split the K steps (wave w takes steps w,
+// w+NWAVE, ...), each loading its share of the 2*NT packed 1 KB blocks per
+// step straight into MFMA operand registers (no LDS), DEPTH steps ahead.  The
+// partial sums meet in LDS and are added in wave order, then the epilogue is
+// the one of the tiled kernel: scales in registers, one store per output.
+// Operand loads past the data (rows >= T, K >= Ci, columns >= Co, steps >=
+// the last) are range-checked to zero.
+template <int MT, int NT, int NWAVE, int DEPTH, bool FUSED>
+__global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
+    const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
+    const uint8_t* __restrict__ wp, int64_t Kp, const float* __restrict__ dw,
+    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo) {
+    static_assert(NWAVE * NT * MT * 16 * 64 * 4 <= 160 * 1024, "partial sums exceed LDS");
+    __shared__ float red[NWAVE][NT * MT][16][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 31, lg = lane >> 5;
+    const int64_t n0 = (int64_t)blockIdx.x * (32 * NT);
+    const int nks = (int)(Kp / BK);
+    const int g0 = (int)(n0 >> 4);                      // first 16-column block
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(qx, (uint32_t)(T * ldq));
+    const int64_t gblocks = (Co >> 4) - g0;             // packed blocks left from g0
+    const int gb = gblocks < 2 * NT ? (int)gblocks : 2 * NT;
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(wp + (int64_t)g0 * nks * 1024, (uint32_t)(gb * nks * 1024));
+
+    // B operand of column tile j: column l%32 -> block 2j + l%32/16, row r in
+    // the block; logical chunks 2*(l/32) and 2*(l/32)+1 of the step, at their
+    // packed units.
+    const int r = lr & 15;
+    uint32_t b_lo[NT], b_hi[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int blk = 2 * j + (lr >> 4);
+        b_lo[j] = (uint32_t)(blk * nks * 1024 + (4 * r + ((2 * lg) ^ ((r >> 2) & 3))) * 16);
+        b_hi[j] = (uint32_t)(blk * nks * 1024 + (4 * r + ((2 * lg + 1) ^ ((r >> 2) & 3))) * 16);
+    }
+    // A operand: token row i*32 + l%32, 32 bytes at 32*(l/32) of the step.
+    uint32_t a_base[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int64_t t = i * 32 + lr;
+        a_base[i] = (t < T) ? (uint32_t)(t * ldq + 32 * lg) : kOutOfRange;
+    }
+
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    v4i fb[DEPTH][NT][2], fa[DEPTH][MT][2];
+    auto load = [&](int slot_u, int ks) {
+        const bool kin = ks < nks;
+        const uint32_t kb = (uint32_t)ks * 1024u;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            fb[slot_u][j][0] =
+                __builtin_amdgcn_raw_buffer_load_b128(rb, kin ? b_lo[j] + kb : kOutOfRange, 0, 0);
+            fb[slot_u][j][1] =
+                __builtin_amdgcn_raw_buffer_load_b128(rb, kin ? b_hi[j] + kb : kOutOfRange, 0, 0);
+        }
+        const int64_t k = (int64_t)ks * BK + 32 * lg;    // this lane's 32 A bytes start here
+        const bool ain = kin && k < Ci;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const bool ok = ain && a_base[i] != kOutOfRange;
+            const uint32_t off = ok ? a_base[i] + (uint32_t)ks * BK : kOutOfRange;
+            fa[slot_u][i][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+            fa[slot_u][i][1] = __builtin_amdgcn_raw_buffer_load_b128(
+                ra, (ok && k + 16 < Ci) ? off + 16 : kOutOfRange, 0, 0);
+        }
+    };
+
+    v16f acc[NT][MT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+
+    const int count = (nks - wave + NWAVE - 1) / NWAVE;  // steps of this wave
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) load(u, wave + NWAVE * u);
+    for (int it = 0; it < count; it += DEPTH) {
+#pragma unroll
+        for (int u = 0; u < DEPTH; ++u) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const v8i bf = v8i{fb[u][j][0].x, fb[u][j][0].y, fb[u][j][0].z, fb[u][j][0].w,
+                                   fb[u][j][1].x, fb[u][j][1].y, fb[u][j][1].z, fb[u][j][1].w};
+#pragma unroll
+                for (int i = 0; i < MT; ++i) {
+                    const v8i af =
+                        v8i{fa[u][i][0].x, fa[u][i][0].y, fa[u][i][0].z, fa[u][i][0].w,
+                            fa[u][i][1].x, fa[u][i][1].y, fa[u][i][1].z, fa[u][i][1].w};
+                    acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bf, af, acc[j][i], 0, 0, 0, 0, 0, 0);
+                }
+            }
+            load(u, wave + NWAVE * (it + u + DEPTH));
+        }
+    }
+
+    // Sum the partials in wave order.  The (column tile, row tile, 4-column
+    // run) triples are dealt round-robin to the waves: run g of tile (j, i)
+    // covers columns 32j + 8g + 4*(l/32) + 0..3 of the workgroup's, token
+    // row 32i + l%32.
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) red[wave][j * MT + i][e][lane] = acc[j][i][e];
+    __syncthreads();
+    for (int p = wave; p < NT * MT * 4; p += NWAVE) {
+        const int ji = p >> 2, g = p & 3;
+        const int j = ji / MT, i = ji - j * MT;
+        const int64_t row = i * 32 + lr;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * g + q;
+            float sum = red[0][ji][e][lane];
+#pragma unroll
+            for (int w = 1; w < NWAVE; ++w) sum += red[w][ji][e][lane];
+            v[q] = sum;
+        }
+        const int64_t c = n0 + 32 * j + 8 * g + 4 * lg;
+        if (row >= T || c >= Co) continue;
+        if constexpr (FUSED) {
+            const float sx = dx[row];
+            const float4 sw = *reinterpret_cast<const float4*>(dw + c);
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16_rne((v[0] * sx) * sw.x) |
+                   ((uint32_t)f32_to_bf16_rne((v[1] * sx) * sw.y) << 16);
+            pk.y = (uint32_t)f32_to_bf16_rne((v[2] * sx) * sw.z) |
+                   ((uint32_t)f32_to_bf16_rne((v[3] * sx) * sw.w) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + row * ldo + c) = pk;
+        } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * Co + c) =
+                make_float4(v[0], v[1], v[2], v[3]);
+        }
+    }
+}
+
+template <int MT, int NT, int NWAVE, int DEPTH>
+static hipError_t launch_decode(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
+                                const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
+                                int64_t ldo, float* fp32_out, hipStream_t s) {
+    const dim3 grid((unsigned)((Co + 32 * NT - 1) / (32 * NT)));
+    const int64_t Kp = round_up_k(Ci);
+    if (fp32_out == nullptr) {
+        hipLaunchKernelGGL((gemm_decode_kernel<MT, NT, NWAVE, DEPTH, true>), grid,
+                           dim3(NWAVE * 64), 0, s, qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out,
+                           ldo);
+    } else {
+        hipLaunchKernelGGL((gemm_decode_kernel<MT, NT, NWAVE, DEPTH, false>), grid,
+                           dim3(NWAVE * 64), 0, s, qx, ldq, dx, wp, Kp, dw, T, Ci, Co,
+                           (void*)fp32_out, Co);
+    }
+    return hipGetLastError();
+}
+
 // Step 2 of the two-step form: read the fp32 GEMM result back and scale.
 __global__ __launch_bounds__(256) void rescale_kernel(const float* __restrict__ ws,
                                                       const float* __restrict__ dx,
@@ -400,15 +563,31 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
     auto rounds = [](int64_t tiles) { return (tiles + kCus - 1) / kCus; };
     const int64_t t256 = ((T + 255) / 256) * ((Co + 255) / 256);
     const int64_t t128 = ((T + 255) / 256) * ((Co + 127) / 128);
+    // Up to 64 tokens the weight stream decides.  The tiled kernel reads
+    // each weight byte once per row tile and keeps the activation in LDS, but
+    // with few column tiles it leaves CUs idle; the few-token kernel splits K
+    // inside a workgroup instead.  It is taken unless the tiled grid has at
+    // least two workgroups per CU (32x64 tiles) or one (128x128 tiles): the
+    // crossover measured on the 8B / 70B projection shapes.  Its 64-column
+    // form (half the activation re-reads) pays off from 16 tokens on, once
+    // the 32-column grid no longer fits the CUs in one round.
     hipError_t e;
     if (T >= 256 && 10 * rounds(t128) * 5 < 9 * rounds(t256) * 10)
         e = launch_tiles<256, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
     else if (T >= 256)
         e = launch_tiles<256, 256, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
-    else if (T > 32)
+    else if (T > 64 || (T > 32 && (Co + 127) / 128 >= kCus))
         e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
-    else
+    else if (T > 32 && (Co + 31) / 32 > kCus)
+        e = launch_decode<2, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+    else if (T > 32)
+        e = launch_decode<2, 1, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+    else if (T > 8 && (Co + 63) / 64 >= 2 * kCus)
         e = launch_tiles<32, 64, 1, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+    else if (T > 8 && (Co + 31) / 32 > kCus)
+        e = launch_decode<1, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+    else
+        e = launch_decode<1, 1, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
     if (e != hipSuccess || fp32_out == nullptr) return e;
     const int64_t n = T * (Co / 4);
     int64_t blocks = (n + 255) / 256;

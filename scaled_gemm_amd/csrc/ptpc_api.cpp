@@ -89,11 +89,17 @@ ptpc_status ptpc_unpack_weight(const void* w_packed, int64_t Ci, int64_t Co, uin
                                                as_stream(stream)));
 }
 
+constexpr int64_t kMaxGemmK = int64_t(1) << 22;
+
 static ptpc_status check_gemm(const uint8_t* qx, int64_t ldq, const float* dx,
                               const void* w_packed, const float* dw, int64_t T, int64_t Ci,
                               int64_t Co, const void* out, int64_t ldo) {
     if (T < 0 || Ci < 0 || Co < 0 || ldq < Ci || ldo < Co) return PTPC_ERR_SHAPE;
     if (Ci % 16 != 0 || Co % 16 != 0) return PTPC_ERR_UNSUPPORTED;
+    // The kernels address an activation tile (<= 256 rows of ldq bytes) and a
+    // weight slab (<= 256 columns of roundup(Ci, 128) bytes) with 32-bit
+    // buffer offsets below 2^31.
+    if (ldq > kMaxGemmK || Ci > kMaxGemmK) return PTPC_ERR_UNSUPPORTED;
     if (T == 0 || Co == 0) return PTPC_OK;
     if (dx == nullptr || dw == nullptr || out == nullptr ||
         (Ci > 0 && (qx == nullptr || w_packed == nullptr)))

@@ -113,6 +113,8 @@ def test_gemm_validation(L):
         assert f(A, 256, B, C, D, 4, 256, 512, NULL, 512) == 1
         assert f(MIS, 256, B, C, D, 4, 256, 512, E, 512) == 4
         assert f(A, 256, B, C, D, 4, 256, 512, E, 516) == 4
+        assert f(A, (1 << 22) + 16, B, C, D, 4, 256, 512, E, 512) == 3
+        assert f(A, (1 << 22) + 16, B, C, D, 4, (1 << 22) + 16, 512, E, 512) == 3
     assert L.ptpc_gemm_unfused(A, 256, B, C, D, 4, 256, 512, E, 512, NULL, None) == 1
     assert L.ptpc_gemm_unfused(A, 256, B, C, D, 4, 256, 512, E, 512, MIS, None) == 4
 

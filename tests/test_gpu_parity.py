@@ -85,6 +85,10 @@ FULL_CASES = [
     ("ragged", 1, 16, 16),
     ("ragged", 3, 144, 48),
     ("ragged", 33, 272, 2064),
+    ("ragged", 97, 400, 1040),
+    ("ragged", 48, 272, 10256),
+    ("ragged", 20, 144, 32784),
+    ("ragged", 24, 208, 8208),
     ("ragged", 600, 256, 2048),
     ("ragged", 513, 512, 2064),
 ]
@@ -280,11 +284,12 @@ def test_pitched_inputs_and_outputs():
     assert np.all(o[:, Co:] == 0)
 
 
-def test_power_of_two_row_scaling_and_permutation():
+@pytest.mark.parametrize("reps", [6, 12])
+def test_power_of_two_row_scaling_and_permutation(reps):
     """Scaling a token by 2^k scales its output by exactly 2^k; permuting
     tokens permutes output rows bit-for-bit."""
     _, x, w = workloads.make("tiny")
-    x = np.concatenate([x] * 12)                       # 192 rows
+    x = np.concatenate([x] * reps)                     # 96 or 192 rows
     rng = np.random.default_rng(0)
     pw = sg.quant_weight(bits_to_dev(w))
     base = dev_to_bits(sg.linear(bits_to_dev(x), pw))
