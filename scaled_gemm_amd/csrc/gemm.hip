@@ -89,8 +89,11 @@ __device__ __forceinline__ void tile_of(int gm, int gn, int& tm, int& tn) {
     const int first_n = group * kGroupN;
     const int width = (gn - first_n < kGroupN) ? gn - first_n : kGroupN;
     const int r = i - group * kGroupN * gm;
-    tm = r / width;
-    tn = first_n + r % width;
+    // The divisions run on the vector ALU; say that the results are the same
+    // in every lane so that the buffer descriptors built from them stay
+    // scalar (a descriptor in vector registers costs a loop per load).
+    tm = __builtin_amdgcn_readfirstlane(r / width);
+    tn = __builtin_amdgcn_readfirstlane(first_n + r % width);
 }
 
 // The pipeline.  K advances in 64-byte steps; each step is one MFMA K
