@@ -321,33 +321,73 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     // Epilogue.  The weight slab is the MFMA's first operand, so the 32x32
     // accumulator tile is out^T: in lane l, element e holds output row
     // (token) l%32 of the slab and output column 8*(e/4) + 4*(l/32) + e%4.
-    // Each lane therefore owns runs of 4 consecutive columns of one row:
-    // 8-byte bf16 stores (16-byte fp32 stores in the two-step form).
+    // Each lane therefore owns runs of 4 consecutive columns of one row.
+    if constexpr (FUSED) {
+        // The bf16 results of one 32-row slab of the wave tile go to a
+        // wave-private LDS region (in the first A slot, idle now) and come
+        // back as 16-byte row chunks, so that every store instruction writes
+        // whole row segments of WTN*2 bytes.  Chunk c of slab row r sits at
+        // chunk c ^ ((r / RB) % NC) of its LDS row (RB rows span the 64
+        // banks), which spreads the 8-byte writes of one instruction (32
+        // rows, one column run) over all banks.
+        constexpr int P = WTN * 2;                   // bytes per slab row
+        constexpr int NC = WTN / 8;                  // 16-byte chunks per row
+        constexpr int RB = 256 / P;
+        constexpr int RPI = 64 / NC;                 // rows per read instruction
+        static_assert(NW * 32 * P <= A_SLOT && RB >= 1 && RPI >= 1, "staging");
+        uint8_t* const stage = a_s0 + wave * (32 * P);
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int64_t row = m0 + wm * WTM + i * 32 + lr;
-        if (row >= T) continue;
-        const float sx = FUSED ? dx[row] : 0.0f;
+        for (int i = 0; i < MT; ++i) {
+            const int64_t row = m0 + wm * WTM + i * 32 + lr;
+            const float sx = (row < T) ? dx[row] : 0.0f;
+            const int sw_r = (lr / RB) % NC;
 #pragma unroll
-        for (int j = 0; j < NTL; ++j) {
+            for (int j = 0; j < NTL; ++j) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t col = n0 + wn * WTN + j * 32 + 8 * g + 4 * lg;
-                if (col >= Co) continue;                  // Co % 16 == 0: runs are whole
-                const float a0 = acc[i][j][4 * g + 0], a1 = acc[i][j][4 * g + 1];
-                const float a2 = acc[i][j][4 * g + 2], a3 = acc[i][j][4 * g + 3];
-                if constexpr (FUSED) {
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t col = n0 + wn * WTN + j * 32 + 8 * g + 4 * lg;
+                    if (row >= T || col >= Co) continue;  // Co % 16 == 0: runs are whole
+                    const float a0 = acc[i][j][4 * g + 0], a1 = acc[i][j][4 * g + 1];
+                    const float a2 = acc[i][j][4 * g + 2], a3 = acc[i][j][4 * g + 3];
                     const float4 sw = *reinterpret_cast<const float4*>(dw + col);
                     uint2 pk;
                     pk.x = (uint32_t)f32_to_bf16_rne((a0 * sx) * sw.x) |
                            ((uint32_t)f32_to_bf16_rne((a1 * sx) * sw.y) << 16);
                     pk.y = (uint32_t)f32_to_bf16_rne((a2 * sx) * sw.z) |
                            ((uint32_t)f32_to_bf16_rne((a3 * sx) * sw.w) << 16);
-                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + row * ldo + col) =
-                        pk;
-                } else {
+                    const int c = 4 * j + g;
+                    *reinterpret_cast<uint2*>(stage + lr * P + ((c ^ sw_r) << 4) + lg * 8) = pk;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+            for (int q = 0; q < 32 / RPI; ++q) {
+                const int rr = q * RPI + lane / NC, cc = lane % NC;
+                const uint4 v = *reinterpret_cast<const uint4*>(
+                    stage + rr * P + ((cc ^ ((rr / RB) % NC)) << 4));
+                const int64_t grow = m0 + wm * WTM + i * 32 + rr;
+                const int64_t gcol = n0 + wn * WTN + cc * 8;
+                if (grow < T && gcol < Co)
+                    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + grow * ldo +
+                                              gcol) = v;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
+    } else {
+        // Two-step form: unscaled fp32 runs of 4 columns, 16-byte stores.
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const int64_t row = m0 + wm * WTM + i * 32 + lr;
+            if (row >= T) continue;
+#pragma unroll
+            for (int j = 0; j < NTL; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int64_t col = n0 + wn * WTN + j * 32 + 8 * g + 4 * lg;
+                    if (col >= Co) continue;
                     *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * Co + col) =
-                        make_float4(a0, a1, a2, a3);
+                        make_float4(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
+                                    acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
                 }
             }
         }
@@ -562,7 +602,8 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
                        int64_t ldo, float* fp32_out, hipStream_t s) {
     // Tile choice: 256x256 keeps the most MFMA work per loaded byte; when it
     // leaves CUs idle or a badly filled last round, 256x128 (twice the tiles,
-    // about 10% less efficient per tile) is taken if its rounds cost less.
+    // each costing about 0.6 of a 256x256 one) is taken if its rounds cost
+    // less.
     auto rounds = [](int64_t tiles) { return (tiles + kCus - 1) / kCus; };
     const int64_t t256 = ((T + 255) / 256) * ((Co + 255) / 256);
     const int64_t t128 = ((T + 255) / 256) * ((Co + 127) / 128);
@@ -575,7 +616,7 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
     // form (half the activation re-reads) pays off from 16 tokens on, once
     // the 32-column grid no longer fits the CUs in one round.
     hipError_t e;
-    if (T >= 256 && 10 * rounds(t128) * 5 < 9 * rounds(t256) * 10)
+    if (T >= 256 && 3 * rounds(t128) < 5 * rounds(t256))
         e = launch_tiles<256, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
     else if (T >= 256)
         e = launch_tiles<256, 256, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
