@@ -321,6 +321,20 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    # A plain device copy (torch copy_, 512 MiB read + 512 MiB written) as the
+    # practical HBM ceiling next to the 8 TB/s peak.
+    cp_src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    cp_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cp_ev[0].record(stream)
+    for _ in range(5):
+        cp_dst.copy_(cp_src)
+    cp_ev[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2.0 * cp_src.numel() / (cp_ev[0].elapsed_time(cp_ev[1]) * 1e-3) / 1e9
+    del cp_src, cp_dst
+
     per_stage = {s: [] for s in stages}
     for ev in events:
         for i, s in enumerate(stages):
@@ -379,6 +393,8 @@ def main():
             "bound": "hbm", "achieved": round(act_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(act_gbs / PEAK_HBM_GBS, 4), "avg_launch_ms": round(avg["quant_act"], 4),
             "bytes_per_launch": act_bytes,
+            "device_copy_gbs": round(copy_gbs, 1),
+            "frac_of_device_copy": round(act_gbs / copy_gbs, 4),
         },
         "stages_ms_avg": {k: round(v, 4) for k, v in avg.items()},
         "stages_ms_median": {k: round(v, 4) for k, v in med.items()},

@@ -44,6 +44,7 @@ def _declare(L):
     L.orc_quant_act.argtypes = [_P, _I, _I, _I, _P, _I, _P]
     L.orc_quant_weight.argtypes = [_P, _I, _I, _I, _P, _I, _P]
     L.orc_quant_tensor.argtypes = [_P, _I, _I, _I, _P, _I, _P]
+    L.orc_quant_static.argtypes = [_P, _I, _I, _I, ctypes.c_float, _P, _I]
     L.orc_gemm_exact.argtypes = [_P, _I, _P, _I, _I, _I, _I, _P]
     L.orc_gemm_exact_i64.argtypes = [_P, _I, _P, _I, _I, _I, _I, _P]
     L.orc_gemm_exact_sampled.argtypes = [_P, _I, _P, _I, _I, _P, _P, _I, _P]
@@ -128,6 +129,15 @@ def quant_tensor(x):
     d = np.empty(1, dtype=np.float32)
     lib().orc_quant_tensor(_ptr(x), R, C, C, _ptr(q), C, _ptr(d))
     return q, d[0]
+
+
+def quant_static(x, s):
+    """Static per-tensor quantization with the given scalar scale s."""
+    x = _c(x, np.uint16)
+    R, C = x.shape
+    q = np.empty((R, C), dtype=np.uint8)
+    lib().orc_quant_static(_ptr(x), R, C, C, ctypes.c_float(float(s)), _ptr(q), C)
+    return q
 
 
 # -- contraction and scales ------------------------------------------------------

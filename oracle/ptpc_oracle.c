@@ -221,6 +221,20 @@ void orc_quant_tensor(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
             q[i * ldq + j] = orc_e4m3_encode(orc_bf16_to_f32(x[i * ldx + j]) / s);
 }
 
+/* Static per-tensor FP8: one scale s fixed ahead of time (from calibration)
+ * rather than measured on the tensor being quantized -- the "standard FP8"
+ * comparator of [PTPC] (§PTPC: a precision-targeted scheme, the per-tensor
+ * baseline; §Benchmark 1) with its scalar scale given.  code =
+ * E4M3(fp32(x) / s), saturating at +-448 like every cast here. */
+void orc_quant_static(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float s,
+                      uint8_t* q, int64_t ldq) {
+    int64_t i, j;
+#pragma omp parallel for schedule(static) private(j)
+    for (i = 0; i < R; ++i)
+        for (j = 0; j < C; ++j)
+            q[i * ldq + j] = orc_e4m3_encode(orc_bf16_to_f32(x[i * ldx + j]) / s);
+}
+
 /* ---------------------------------------------------------------------
  * The FP8 x FP8 contraction ([PTPC] §The challenge: two-step vs fused,
  * step 1 of the naive code): acc[t,o] = sum_k dec(qx[t,k]) * dec(qw[k,o]).

@@ -43,6 +43,9 @@ void orc_quant_weight(const uint16_t* w, int64_t Ci, int64_t Co, int64_t ldw,
                       uint8_t* qw, int64_t ldqw, float* dw);
 void orc_quant_tensor(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
                       uint8_t* q, int64_t ldq, float* d);
+/* Static per-tensor: codes for a given scalar scale s (> 0). */
+void orc_quant_static(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, float s,
+                      uint8_t* q, int64_t ldq);
 
 /* --- exact FP8 contraction ------------------------------------------- */
 void orc_gemm_exact(const uint8_t* qx, int64_t ldq, const uint8_t* qw,

@@ -10,6 +10,16 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [base, base + bytes): loads at offsets past
+// `bytes` return zero instead of touching memory.
+constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kBufferDword3);
+}
+constexpr int kCacheNonTemporal = 2;        // buffer-load cache policy: nt
 
 // bf16 bit patterns packed two to a 32-bit word: low half is the element at
 // the lower address.

@@ -36,7 +36,6 @@
 namespace ptpc {
 
 constexpr int BK = 64;          // K bytes per step (one MFMA K step)
-constexpr int kBufferDword3 = 0x00020000;   // raw buffer, 32-bit data format
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // LDS bank swizzles (64 banks of 4 bytes; an operand read has 16 consecutive
@@ -49,11 +48,6 @@ __device__ __forceinline__ int swz_b(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 7; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             kBufferDword3);
-}
 
 // Workgroup barrier without the release/acquire fences of __syncthreads():
 // the fence would wait for every load in flight into LDS (vmcnt 0), which
@@ -442,7 +436,6 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
         a_base[i] = (t < T) ? (uint32_t)(t * ldq + 32 * lg) : kOutOfRange;
     }
 
-    typedef int v4i __attribute__((ext_vector_type(4)));
     v4i fb[DEPTH][NT][2], fa[DEPTH][MT][2];
     auto load = [&](int slot_u, int ks) {
         const bool kin = ks < nks;

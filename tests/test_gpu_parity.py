@@ -178,7 +178,7 @@ def test_quant_act_exhaustive_pairs():
     input the quantizer can see (rows of various lengths exercise each
     launch shape)."""
     amax_all = np.arange(1, 0x7F80, dtype=np.int32)       # positive finite bf16
-    buckets = [512, 1024, 2048, 4096, 8192, 16384, 32768]
+    buckets = [512, 1024, 2048, 4096, 8192, 16384, 24576, 28672, 32768]
     total = 0
     lo = 0
     for Ci in buckets:

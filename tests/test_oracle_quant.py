@@ -179,3 +179,39 @@ def test_weight_quant_is_act_quant_of_transpose(orc):
     assert dw.shape == (80,)
     assert np.array_equal(dw, dt)
     assert np.array_equal(qw, qt.T)
+
+
+# -- static per-tensor (the "standard FP8" comparator with a given scale) -----
+def test_static_with_measured_scale_is_per_tensor(orc):
+    """Given the scale the per-tensor quantizer measures, static quantization
+    reproduces its codes."""
+    rng = np.random.default_rng(21)
+    x = workloads.random_bf16(rng, 33, 272, 1.5)
+    q_ten, d_ten = orc.quant_tensor(x)
+    assert np.array_equal(orc.quant_static(x, d_ten), q_ten)
+
+
+def test_static_scale_one_is_torch_cast(orc):
+    """s = 1: every code is the plain cast of the bf16 value (within +-448,
+    where PyTorch's float8_e4m3fn cast is defined without saturation)."""
+    b = np.arange(1 << 16, dtype=np.uint32)
+    vals = (b << 16).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 448)]
+    n = 1024
+    pad = np.zeros(-(-vals.size // n) * n, F32)
+    pad[:vals.size] = vals
+    m = pad.reshape(-1, n)
+    x = workloads.f32_to_bf16_bits(m)
+    want = torch.from_numpy(m.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.quant_static(x, 1.0), want)
+
+
+def test_static_saturates_beyond_range(orc):
+    """A static scale can be too small for the data: quotients beyond 448
+    (464 included, the tie between 448 and the next binade) saturate to the
+    largest finite code, sign kept; NaN codes never appear."""
+    v = np.array([[449.0, 464.0, 465.0, 1e6, -449.0, -464.0, -1e6, 3.0e38]], F32)
+    q = orc.quant_static(workloads.f32_to_bf16_bits(v), 1.0)
+    assert q.tolist() == [[0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0xFE, 0x7E]]
+    q2 = orc.quant_static(workloads.f32_to_bf16_bits(np.array([[8.0, -8.0, -0.5]], F32)), 2.0 ** -6)
+    assert q2.tolist() == [[0x7E, 0xFE, 0xE0]]            # -0.5 / 2^-6 = -32 is in range
