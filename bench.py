@@ -321,6 +321,34 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    # The per-tensor comparator on the same inputs (not part of the step):
+    # dynamic per-tensor activation scale + static cast, and the GEMM with
+    # scalar scales; the weight is quantized per tensor once, outside.
+    pt = None
+    if not args.only:
+        sw_t = sg.tensor_scale(w)
+        pw_t = sg.quant_weight_static(w, sw_t)
+        sx_t = torch.empty((1,), dtype=torch.float32, device=dev)
+        qx_t = torch.empty_like(qx)
+        out_t = torch.empty_like(out)
+        pt_calls = [("tensor_scale", lambda: sg.tensor_scale(x, d=sx_t)),
+                    ("quant_act_static", lambda: sg.quant_act_static(x, sx_t, qx=qx_t)),
+                    ("gemm_tensor", lambda: sg.gemm_tensor(qx_t, sx_t, pw_t, out=out_t))]
+        for _ in range(3):
+            for _, fn in pt_calls:
+                fn()
+        pt_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                 for _ in range(args.steps)]
+        for k in range(args.steps):
+            for i, (_, fn) in enumerate(pt_calls):
+                pt_ev[k][i].record(stream)
+                fn()
+            pt_ev[k][3].record(stream)
+        torch.cuda.synchronize()
+        pt = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in pt_ev]))
+              for i, (name, _) in enumerate(pt_calls)}
+        del sw_t, pw_t, sx_t, qx_t, out_t
+
     # A plain device copy (torch copy_, 512 MiB read + 512 MiB written) as the
     # practical HBM ceiling next to the 8 TB/s peak.
     cp_src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -404,6 +432,16 @@ def main():
                                if {"gemm_fused", "gemm_unfused"} <= run else None),
         "cpu_baseline": None,
     }
+    if pt is not None:
+        result["per_tensor"] = {
+            "what": "per-tensor FP8 comparator on the same inputs: tensor_scale(X) + "
+                    "quant_act_static + gemm_tensor (weight quantized per tensor once)",
+            "ms_avg": {k: round(v, 4) for k, v in pt.items()},
+            "gemm_tensor_tflops": round(gemm_flops / (pt["gemm_tensor"] * 1e-3) / 1e12, 1),
+            "ptpc_over_per_tensor_gemm_time": round(avg["gemm_fused"] / pt["gemm_tensor"], 4),
+            "ptpc_over_per_tensor_act_quant_time": round(
+                avg["quant_act"] / (pt["tensor_scale"] + pt["quant_act_static"]), 4),
+        }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -138,6 +138,39 @@ ptpc_status ptpc_gemm_unfused(const uint8_t* qx, int64_t ldq, const float* dx,
                               int64_t Ci, int64_t Co, void* out, int64_t ldo,
                               float* workspace, void* stream);
 
+/*
+ * ---- Per-tensor ("standard") FP8, the comparator ------------------------
+ * [PTPC] measures PTPC-FP8 against FP8 with one scale per tensor
+ * (§PTPC: a precision-targeted scheme; §Benchmark 1 throughput,
+ * §Benchmark 2.1/2.2 accuracy).  These calls give that baseline on the same
+ * kernels: a scalar scale per matrix, measured (ptpc_tensor_scale) or given
+ * ahead of time ("static", e.g. from calibration).  Same conventions and
+ * contract as above; a scale argument is a device pointer to ONE fp32.
+ */
+
+/* d[0] = max |x| / 448 over the R x C bf16 matrix x (pitch ld), or 1 if it
+ * is all zero or empty.  Works for activations ([T x Ci]) and weights
+ * ([Ci x Co]) alike.  C % 16 == 0. */
+ptpc_status ptpc_tensor_scale(const void* x, int64_t R, int64_t C, int64_t ld, float* d,
+                              void* stream);
+
+/* qx[t,k] = E4M3(x[t,k] / d[0]) (saturating at +-448), x [T x Ci] bf16, qx
+ * E4M3 codes; d[0] > 0 is read, not written. */
+ptpc_status ptpc_quant_act_static(const void* x, int64_t T, int64_t Ci, int64_t ldx,
+                                  const float* d, uint8_t* qx, int64_t ldq, void* stream);
+
+/* Quantize W [Ci x Co] with the scalar scale d[0] and prepack it into the
+ * layout of ptpc_quant_weight (same size, same ptpc_unpack_weight). */
+ptpc_status ptpc_quant_weight_static(const void* w, int64_t Ci, int64_t Co, int64_t ldw,
+                                     const float* d, void* w_packed, void* stream);
+
+/* ptpc_gemm with scalar scales: out[t,o] = bf16((acc[t,o] * dx[0]) * dw[0]);
+ * dx and dw point to one fp32 each. */
+ptpc_status ptpc_gemm_tensor(const uint8_t* qx, int64_t ldq, const float* dx,
+                             const void* w_packed, const float* dw, int64_t T,
+                             int64_t Ci, int64_t Co, void* out, int64_t ldo,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

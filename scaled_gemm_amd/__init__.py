@@ -26,7 +26,8 @@ _STATUS = {
 EXPORTS = (
     "ptpc_status_string", "ptpc_abi_version", "ptpc_quant_act", "ptpc_weight_packed_bytes",
     "ptpc_quant_weight", "ptpc_unpack_weight", "ptpc_gemm",
-    "ptpc_gemm_unfused_workspace_bytes", "ptpc_gemm_unfused",
+    "ptpc_gemm_unfused_workspace_bytes", "ptpc_gemm_unfused", "ptpc_tensor_scale",
+    "ptpc_quant_act_static", "ptpc_quant_weight_static", "ptpc_gemm_tensor",
 )
 
 _lib = None
@@ -65,6 +66,14 @@ def lib():
         L.ptpc_gemm_unfused_workspace_bytes.argtypes = [I, I]
         L.ptpc_gemm_unfused.restype = ctypes.c_int
         L.ptpc_gemm_unfused.argtypes = [P, I, P, P, P, I, I, I, P, I, P, P]
+        L.ptpc_tensor_scale.restype = ctypes.c_int
+        L.ptpc_tensor_scale.argtypes = [P, I, I, I, P, P]
+        L.ptpc_quant_act_static.restype = ctypes.c_int
+        L.ptpc_quant_act_static.argtypes = [P, I, I, I, P, P, I, P]
+        L.ptpc_quant_weight_static.restype = ctypes.c_int
+        L.ptpc_quant_weight_static.argtypes = [P, I, I, I, P, P, P]
+        L.ptpc_gemm_tensor.restype = ctypes.c_int
+        L.ptpc_gemm_tensor.argtypes = [P, I, P, P, P, I, I, I, P, I, P]
         _lib = L
     return _lib
 
@@ -173,3 +182,53 @@ def linear(x, pw: PackedWeight, stream=None):
     """Per-token quantization of X followed by the fused GEMM (one layer's forward)."""
     qx, dx = quant_act(x, stream=stream)
     return gemm(qx, dx, pw, stream=stream)
+
+
+# -- per-tensor comparator ------------------------------------------------------
+def tensor_scale(x, d=None, stream=None):
+    """One scale for a whole bf16 matrix: d[0] = max|x| / 448 (1 if zero) -> fp32 [1]."""
+    R, C, ld = _matrix(x, torch.bfloat16, "x")
+    if d is None:
+        d = torch.empty((1,), dtype=torch.float32, device=x.device)
+    _check("ptpc_tensor_scale", lib().ptpc_tensor_scale(_ptr(x), R, C, ld, _ptr(d),
+                                                        _stream(stream)))
+    return d
+
+
+def quant_act_static(x, d, qx=None, stream=None):
+    """Per-tensor FP8 codes of bf16 X [T, Ci] with the given scale d (fp32 [1])."""
+    T, Ci, ldx = _matrix(x, torch.bfloat16, "x")
+    if qx is None:
+        qx = torch.empty((T, Ci), dtype=torch.uint8, device=x.device)
+    _, _, ldq = _matrix(qx, torch.uint8, "qx")
+    _check("ptpc_quant_act_static",
+           lib().ptpc_quant_act_static(_ptr(x), T, Ci, ldx, _ptr(d), _ptr(qx), ldq,
+                                       _stream(stream)))
+    return qx
+
+
+def quant_weight_static(w, d, out: PackedWeight = None, stream=None) -> PackedWeight:
+    """Per-tensor FP8 codes of bf16 W [Ci, Co] with the scale d (fp32 [1]), prepacked;
+    the returned PackedWeight carries d as its (one-element) dw."""
+    Ci, Co, ldw = _matrix(w, torch.bfloat16, "w")
+    if out is None:
+        out = PackedWeight(torch.empty((packed_bytes(Ci, Co),), dtype=torch.uint8, device=w.device),
+                           d, Ci, Co)
+    _check("ptpc_quant_weight_static",
+           lib().ptpc_quant_weight_static(_ptr(w), Ci, Co, ldw, _ptr(d), _ptr(out.data),
+                                          _stream(stream)))
+    return out
+
+
+def gemm_tensor(qx, dx, pw: PackedWeight, out=None, stream=None):
+    """Per-tensor FP8 GEMM: bf16 [T, Co] = ((qx @ qw) * dx[0]) * dw[0]."""
+    T, Ci, ldq = _matrix(qx, torch.uint8, "qx")
+    if Ci != pw.Ci:
+        raise ValueError(f"qx has Ci={Ci}, weight has Ci={pw.Ci}")
+    if out is None:
+        out = torch.empty((T, pw.Co), dtype=torch.bfloat16, device=qx.device)
+    _, _, ldo = _matrix(out, torch.bfloat16, "out")
+    _check("ptpc_gemm_tensor", lib().ptpc_gemm_tensor(_ptr(qx), ldq, _ptr(dx), _ptr(pw.data),
+                                                      _ptr(pw.dw), T, Ci, pw.Co, _ptr(out), ldo,
+                                                      _stream(stream)))
+    return out

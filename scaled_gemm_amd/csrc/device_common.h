@@ -85,13 +85,25 @@ __device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b, uint32_t old) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, WORD_HI);
 }
 
-// Eight bf16 (one 16-byte vector) divided by one divisor -> eight E4M3 codes.
+// Clamp a quotient to the largest finite E4M3 magnitude.  A scale derived
+// from the data's own amax keeps every quotient within 448 (up to rounding,
+// which the conversion rounds back to 448); a scale given ahead of time can
+// leave quotients far beyond it, which the conversion alone does not
+// saturate.  Quotients within +-448 pass unchanged.
+__device__ __forceinline__ float sat448(float q) {
+    return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f);
+}
+
+// Eight bf16 (one 16-byte vector) divided by one divisor -> eight E4M3 codes
+// (SAT: clamp the quotients first, for given scales).
+template <bool SAT = false>
 __device__ __forceinline__ uint2 quantize8(uint4 v, const Divisor& dv) {
+    auto q = [&](float f) { return SAT ? sat448(divide(f, dv)) : divide(f, dv); };
     uint32_t lo = 0, hi = 0;
-    lo = cvt_e4m3x2<false>(divide(bf16lo_to_f32(v.x), dv), divide(bf16hi_to_f32(v.x), dv), lo);
-    lo = cvt_e4m3x2<true>(divide(bf16lo_to_f32(v.y), dv), divide(bf16hi_to_f32(v.y), dv), lo);
-    hi = cvt_e4m3x2<false>(divide(bf16lo_to_f32(v.z), dv), divide(bf16hi_to_f32(v.z), dv), hi);
-    hi = cvt_e4m3x2<true>(divide(bf16lo_to_f32(v.w), dv), divide(bf16hi_to_f32(v.w), dv), hi);
+    lo = cvt_e4m3x2<false>(q(bf16lo_to_f32(v.x)), q(bf16hi_to_f32(v.x)), lo);
+    lo = cvt_e4m3x2<true>(q(bf16lo_to_f32(v.y)), q(bf16hi_to_f32(v.y)), lo);
+    hi = cvt_e4m3x2<false>(q(bf16lo_to_f32(v.z)), q(bf16hi_to_f32(v.z)), hi);
+    hi = cvt_e4m3x2<true>(q(bf16lo_to_f32(v.w)), q(bf16hi_to_f32(v.w)), hi);
     return make_uint2(lo, hi);
 }
 

@@ -108,7 +108,7 @@ template <int BM, int BN, int WM, int WN, int NB, bool FUSED>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
     const uint8_t* __restrict__ wp, int64_t Kp, const float* __restrict__ dw,
-    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo) {
+    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo, int tensor_scales) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MT = WTM / 32, NTL = WTN / 32;
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             const int64_t row = m0 + wm * WTM + i * 32 + lr;
-            const float sx = (row < T) ? dx[row] : 0.0f;
+            const float sx = (row < T) ? dx[tensor_scales ? 0 : row] : 0.0f;
             const int sw_r = (lr / RB) % NC;
 #pragma unroll
             for (int j = 0; j < NTL; ++j) {
@@ -343,7 +343,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
                     if (row >= T || col >= Co) continue;  // Co % 16 == 0: runs are whole
                     const float a0 = acc[i][j][4 * g + 0], a1 = acc[i][j][4 * g + 1];
                     const float a2 = acc[i][j][4 * g + 2], a3 = acc[i][j][4 * g + 3];
-                    const float4 sw = *reinterpret_cast<const float4*>(dw + col);
+                    const float4 sw = tensor_scales
+                                          ? make_float4(dw[0], dw[0], dw[0], dw[0])
+                                          : *reinterpret_cast<const float4*>(dw + col);
                     uint2 pk;
                     pk.x = (uint32_t)f32_to_bf16_rne((a0 * sx) * sw.x) |
                            ((uint32_t)f32_to_bf16_rne((a1 * sx) * sw.y) << 16);
@@ -401,7 +403,7 @@ template <int MT, int NT, int NWAVE, int DEPTH, bool FUSED>
 __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
     const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
     const uint8_t* __restrict__ wp, int64_t Kp, const float* __restrict__ dw,
-    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo) {
+    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo, int tensor_scales) {
     static_assert(NWAVE * NT * MT * 16 * 64 * 4 <= 160 * 1024, "partial sums exceed LDS");
     __shared__ float red[NWAVE][NT * MT][16][64];
     const int lane = threadIdx.x & 63;
@@ -517,8 +519,9 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
         const int64_t c = n0 + 32 * j + 8 * g + 4 * lg;
         if (row >= T || c >= Co) continue;
         if constexpr (FUSED) {
-            const float sx = dx[row];
-            const float4 sw = *reinterpret_cast<const float4*>(dw + c);
+            const float sx = dx[tensor_scales ? 0 : row];
+            const float4 sw = tensor_scales ? make_float4(dw[0], dw[0], dw[0], dw[0])
+                                            : *reinterpret_cast<const float4*>(dw + c);
             uint2 pk;
             pk.x = (uint32_t)f32_to_bf16_rne((v[0] * sx) * sw.x) |
                    ((uint32_t)f32_to_bf16_rne((v[1] * sx) * sw.y) << 16);
@@ -535,17 +538,17 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
 template <int MT, int NT, int NWAVE, int DEPTH>
 static hipError_t launch_decode(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                                 const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
-                                int64_t ldo, float* fp32_out, hipStream_t s) {
+                                int64_t ldo, float* fp32_out, hipStream_t s, int ts) {
     const dim3 grid((unsigned)((Co + 32 * NT - 1) / (32 * NT)));
     const int64_t Kp = round_up_k(Ci);
     if (fp32_out == nullptr) {
         hipLaunchKernelGGL((gemm_decode_kernel<MT, NT, NWAVE, DEPTH, true>), grid,
                            dim3(NWAVE * 64), 0, s, qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out,
-                           ldo);
+                           ldo, ts);
     } else {
         hipLaunchKernelGGL((gemm_decode_kernel<MT, NT, NWAVE, DEPTH, false>), grid,
                            dim3(NWAVE * 64), 0, s, qx, ldq, dx, wp, Kp, dw, T, Ci, Co,
-                           (void*)fp32_out, Co);
+                           (void*)fp32_out, Co, 0);
     }
     return hipGetLastError();
 }
@@ -577,22 +580,23 @@ __global__ __launch_bounds__(256) void rescale_kernel(const float* __restrict__ 
 template <int BM, int BN, int WM, int WN, int NB>
 static hipError_t launch_tiles(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                                const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
-                               int64_t ldo, float* fp32_out, hipStream_t s) {
+                               int64_t ldo, float* fp32_out, hipStream_t s, int ts) {
     const dim3 grid((unsigned)(((Co + BN - 1) / BN) * ((T + BM - 1) / BM)));
     const int64_t Kp = round_up_k(Ci);
     if (fp32_out == nullptr) {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NB, true>), grid, dim3(WM * WN * 64), 0, s,
-                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out, ldo);
+                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out, ldo, ts);
     } else {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NB, false>), grid, dim3(WM * WN * 64), 0, s,
-                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)fp32_out, Co);
+                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)fp32_out, Co, 0);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                        const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
-                       int64_t ldo, float* fp32_out, hipStream_t s) {
+                       int64_t ldo, float* fp32_out, hipStream_t s, bool per_tensor) {
+    const int ts = per_tensor ? 1 : 0;
     // Tile choice: 256x256 keeps the most MFMA work per loaded byte; when it
     // leaves CUs idle or a badly filled last round, 256x128 (twice the tiles,
     // each costing about 0.6 of a 256x256 one) is taken if its rounds cost
@@ -610,21 +614,21 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
     // the 32-column grid no longer fits the CUs in one round.
     hipError_t e;
     if (T >= 256 && 3 * rounds(t128) < 5 * rounds(t256))
-        e = launch_tiles<256, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_tiles<256, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T >= 256)
-        e = launch_tiles<256, 256, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_tiles<256, 256, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T > 64 || (T > 32 && (Co + 127) / 128 >= kCus))
-        e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T > 32 && (Co + 31) / 32 > kCus)
-        e = launch_decode<2, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_decode<2, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T > 32)
-        e = launch_decode<2, 1, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_decode<2, 1, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T > 8 && (Co + 63) / 64 >= 2 * kCus)
-        e = launch_tiles<32, 64, 1, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_tiles<32, 64, 1, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T > 8 && (Co + 31) / 32 > kCus)
-        e = launch_decode<1, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_decode<1, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else
-        e = launch_decode<1, 1, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s);
+        e = launch_decode<1, 1, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     if (e != hipSuccess || fp32_out == nullptr) return e;
     const int64_t n = T * (Co / 4);
     int64_t blocks = (n + 255) / 256;

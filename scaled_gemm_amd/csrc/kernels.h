@@ -17,14 +17,25 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t Ci, int64_t ld
 hipError_t launch_quant_weight(const uint16_t* w, int64_t Ci, int64_t Co, int64_t ldw,
                                uint8_t* packed, float* dw, hipStream_t s);
 
+// Per-tensor comparator: d[0] = amax / 448 over an R x C bf16 matrix (1 if
+// all zero); static casts with the scalar scale d[0].
+hipError_t launch_tensor_scale(const uint16_t* x, int64_t R, int64_t C, int64_t ld, float* d,
+                               hipStream_t s);
+hipError_t launch_quant_act_static(const uint16_t* x, int64_t T, int64_t Ci, int64_t ldx,
+                                   const float* d, uint8_t* qx, int64_t ldq, hipStream_t s);
+hipError_t launch_quant_weight_static(const uint16_t* w, int64_t Ci, int64_t Co, int64_t ldw,
+                                      const float* d, uint8_t* packed, hipStream_t s);
+
 hipError_t launch_unpack_weight(const uint8_t* packed, int64_t Ci, int64_t Co, uint8_t* qw,
                                 hipStream_t s);
 
 // fp32_out == nullptr: fused epilogue writing bf16 `out`.
 // fp32_out != nullptr: the GEMM stores unscaled fp32 sums there ([T x Co],
 // pitch Co), then a rescale kernel writes bf16 `out`.
+// per_tensor: the fused epilogue uses dx[0] and dw[0] for every row and
+// column (the two-step form is per-token / per-channel only).
 hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                        const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
-                       int64_t ldo, float* fp32_out, hipStream_t s);
+                       int64_t ldo, float* fp32_out, hipStream_t s, bool per_tensor = false);
 
 }  // namespace ptpc

@@ -140,4 +140,56 @@ ptpc_status ptpc_gemm_unfused(const uint8_t* qx, int64_t ldq, const float* dx,
                                       as_stream(stream)));
 }
 
+// ---- per-tensor comparator ---------------------------------------------
+
+ptpc_status ptpc_tensor_scale(const void* x, int64_t R, int64_t C, int64_t ld, float* d,
+                              void* stream) {
+    if (R < 0 || C < 0 || ld < C) return PTPC_ERR_SHAPE;
+    if (C % 16 != 0) return PTPC_ERR_UNSUPPORTED;
+    if (d == nullptr || (R > 0 && C > 0 && x == nullptr)) return PTPC_ERR_NULL;
+    if (!aligned16(d) || (R > 0 && C > 0 && (!aligned16(x) || ld % 8 != 0)))
+        return PTPC_ERR_ALIGN;
+    if (forced_launch_failure()) return PTPC_ERR_HIP;
+    return from_hip(ptpc::launch_tensor_scale(static_cast<const uint16_t*>(x), R, C, ld, d,
+                                              as_stream(stream)));
+}
+
+ptpc_status ptpc_quant_act_static(const void* x, int64_t T, int64_t Ci, int64_t ldx,
+                                  const float* d, uint8_t* qx, int64_t ldq, void* stream) {
+    if (T < 0 || Ci < 0 || ldx < Ci || ldq < Ci) return PTPC_ERR_SHAPE;
+    if (Ci % 16 != 0) return PTPC_ERR_UNSUPPORTED;
+    if (T == 0 || Ci == 0) return PTPC_OK;
+    if (x == nullptr || d == nullptr || qx == nullptr) return PTPC_ERR_NULL;
+    if (!aligned16(x) || !aligned16(d) || !aligned16(qx) || ldx % 8 != 0 || ldq % 16 != 0)
+        return PTPC_ERR_ALIGN;
+    if (forced_launch_failure()) return PTPC_ERR_HIP;
+    return from_hip(ptpc::launch_quant_act_static(static_cast<const uint16_t*>(x), T, Ci, ldx,
+                                                  d, qx, ldq, as_stream(stream)));
+}
+
+ptpc_status ptpc_quant_weight_static(const void* w, int64_t Ci, int64_t Co, int64_t ldw,
+                                     const float* d, void* w_packed, void* stream) {
+    if (Ci < 0 || Co < 0 || ldw < Co) return PTPC_ERR_SHAPE;
+    if (Ci % 16 != 0 || Co % 16 != 0) return PTPC_ERR_UNSUPPORTED;
+    if (Ci == 0 || Co == 0) return PTPC_OK;
+    if (w == nullptr || d == nullptr || w_packed == nullptr) return PTPC_ERR_NULL;
+    if (!aligned16(w) || !aligned16(d) || !aligned16(w_packed) || ldw % 8 != 0)
+        return PTPC_ERR_ALIGN;
+    if (forced_launch_failure()) return PTPC_ERR_HIP;
+    return from_hip(ptpc::launch_quant_weight_static(static_cast<const uint16_t*>(w), Ci, Co,
+                                                     ldw, d, static_cast<uint8_t*>(w_packed),
+                                                     as_stream(stream)));
+}
+
+ptpc_status ptpc_gemm_tensor(const uint8_t* qx, int64_t ldq, const float* dx,
+                             const void* w_packed, const float* dw, int64_t T, int64_t Ci,
+                             int64_t Co, void* out, int64_t ldo, void* stream) {
+    ptpc_status st = check_gemm(qx, ldq, dx, w_packed, dw, T, Ci, Co, out, ldo);
+    if (st != PTPC_OK || T == 0 || Co == 0) return st;
+    if (forced_launch_failure()) return PTPC_ERR_HIP;
+    return from_hip(ptpc::launch_gemm(qx, ldq, dx, static_cast<const uint8_t*>(w_packed), dw, T,
+                                      Ci, Co, static_cast<uint16_t*>(out), ldo, nullptr,
+                                      as_stream(stream), true));
+}
+
 }  // extern "C"

@@ -251,9 +251,11 @@ constexpr int kPackK = 128;
 constexpr int kPackN = 64;
 constexpr int kPackPitch = kPackK + 16;   // keeps 16-byte alignment of rows
 
+// dw_step = 1: column o uses dw[o] (per-channel); 0: every column uses dw[0]
+// (per-tensor).
 __global__ __launch_bounds__(256) void weight_pack_kernel(
     const uint16_t* __restrict__ w, int64_t Ci, int64_t Co, int64_t ldw,
-    const float* __restrict__ dw, uint8_t* __restrict__ packed, int64_t Kp) {
+    const float* __restrict__ dw, int64_t dw_step, uint8_t* __restrict__ packed, int64_t Kp) {
     __shared__ __attribute__((aligned(16))) uint8_t tile[kPackN * kPackPitch];
     const int tid = threadIdx.x;
     const int cg = tid & 7;            // 8-column group within the tile
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(256) void weight_pack_kernel(
 
     Divisor dv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dv[j] = make_divisor(col_ok ? dw[col + j] : 1.0f);
+    for (int j = 0; j < 8; ++j) dv[j] = make_divisor(col_ok ? dw[(col + j) * dw_step] : 1.0f);
 
 #pragma unroll
     for (int p = 0; p < kPackK / 32; ++p) {
@@ -276,8 +278,9 @@ __global__ __launch_bounds__(256) void weight_pack_kernel(
         const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-            uint32_t c = cvt_e4m3x2<false>(divide(bf16lo_to_f32(wd[h]), dv[2 * h]),
-                                           divide(bf16hi_to_f32(wd[h]), dv[2 * h + 1]), 0u);
+            uint32_t c = cvt_e4m3x2<false>(sat448(divide(bf16lo_to_f32(wd[h]), dv[2 * h])),
+                                           sat448(divide(bf16hi_to_f32(wd[h]), dv[2 * h + 1])),
+                                           0u);
             tile[(cg * 8 + 2 * h) * kPackPitch + kl] = (uint8_t)(c & 0xFF);
             tile[(cg * 8 + 2 * h + 1) * kPackPitch + kl] = (uint8_t)((c >> 8) & 0xFF);
         }
@@ -324,8 +327,103 @@ hipError_t launch_quant_weight(const uint16_t* w, int64_t Ci, int64_t Co, int64_
     if (Kp > 0) {
         hipLaunchKernelGGL(weight_pack_kernel,
                            dim3((unsigned)((Co + kPackN - 1) / kPackN), (unsigned)(Kp / kPackK)),
-                           dim3(256), 0, s, w, Ci, Co, ldw, dw, packed, Kp);
+                           dim3(256), 0, s, w, Ci, Co, ldw, dw, (int64_t)1, packed, Kp);
     }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-tensor ("standard") FP8, the comparator: one scale for a whole matrix.
+// The amax pass gives each wave whole rows (16-byte loads along the row),
+// reduces the workgroup in LDS and merges workgroups with one integer
+// atomicMax on the fp32 bit pattern; the scale kernel then converts it in
+// place.  The static casts are plain streams with a scalar divisor.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tensor_amax_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ld, int64_t rows_per_block,
+    uint32_t* __restrict__ amax_bits) {
+    __shared__ uint32_t red[4];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t nvec = C / 8;
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+    int64_t r1 = r0 + rows_per_block;
+    if (r1 > R) r1 = R;
+    us2 m = {0, 0};
+    for (int64_t r = r0 + wave; r < r1; r += 4) {
+        const uint4* xr = reinterpret_cast<const uint4*>(x + r * ld);
+        for (int64_t c = lane; c < nvec; c += 64) {
+            const uint4 v = xr[c];
+            m = max2(m, abs_bits2(v.x));
+            m = max2(m, abs_bits2(v.y));
+            m = max2(m, abs_bits2(v.z));
+            m = max2(m, abs_bits2(v.w));
+        }
+    }
+    const uint32_t w = wave_max_u32(hmax(m));
+    if (lane == 0) red[wave] = w;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t a = red[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) a = a > red[i] ? a : red[i];
+        if (a) atomicMax(amax_bits, a << 16);
+    }
+}
+
+// code = E4M3(x / d[0]) for an R x C bf16 matrix, row pitches ld / ldq.
+__global__ __launch_bounds__(256) void quant_static_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, int64_t ld,
+    const float* __restrict__ d, uint8_t* __restrict__ q, int64_t ldq, int64_t rows_per_block) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t nvec = C / 8;
+    const Divisor dv = make_divisor(d[0]);
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+    int64_t r1 = r0 + rows_per_block;
+    if (r1 > R) r1 = R;
+    for (int64_t r = r0 + wave; r < r1; r += 4) {
+        const uint4* xr = reinterpret_cast<const uint4*>(x + r * ld);
+        uint2* qr = reinterpret_cast<uint2*>(q + r * ldq);
+        for (int64_t c = lane; c < nvec; c += 64) qr[c] = quantize8<true>(xr[c], dv);
+    }
+}
+
+// Rows per workgroup for the row-streaming kernels: about 2048 workgroups,
+// at least 4 rows (one per wave).
+static int64_t rows_per_block_for(int64_t R) {
+    int64_t rpb = (R + 2047) / 2048;
+    if (rpb < 4) rpb = 4;
+    return rpb;
+}
+
+hipError_t launch_tensor_scale(const uint16_t* x, int64_t R, int64_t C, int64_t ld, float* d,
+                               hipStream_t s) {
+    uint32_t* amax_bits = reinterpret_cast<uint32_t*>(d);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, amax_bits, (int64_t)1);
+    if (R > 0 && C > 0) {
+        const int64_t rpb = rows_per_block_for(R);
+        hipLaunchKernelGGL(tensor_amax_kernel, dim3((unsigned)((R + rpb - 1) / rpb)), dim3(256),
+                           0, s, x, R, C, ld, rpb, amax_bits);
+    }
+    hipLaunchKernelGGL(weight_scale_kernel, dim3(1), dim3(64), 0, s, d, (int64_t)1);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_static(const uint16_t* x, int64_t T, int64_t Ci, int64_t ldx,
+                                   const float* d, uint8_t* qx, int64_t ldq, hipStream_t s) {
+    const int64_t rpb = rows_per_block_for(T);
+    hipLaunchKernelGGL(quant_static_kernel, dim3((unsigned)((T + rpb - 1) / rpb)), dim3(256), 0,
+                       s, x, T, Ci, ldx, d, qx, ldq, rpb);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_static(const uint16_t* w, int64_t Ci, int64_t Co, int64_t ldw,
+                                      const float* d, uint8_t* packed, hipStream_t s) {
+    const int64_t Kp = round_up_k(Ci);
+    hipLaunchKernelGGL(weight_pack_kernel,
+                       dim3((unsigned)((Co + kPackN - 1) / kPackN), (unsigned)(Kp / kPackK)),
+                       dim3(256), 0, s, w, Ci, Co, ldw, d, (int64_t)0, packed, Kp);
     return hipGetLastError();
 }
 

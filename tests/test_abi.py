@@ -119,6 +119,34 @@ def test_gemm_validation(L):
     assert L.ptpc_gemm_unfused(A, 256, B, C, D, 4, 256, 512, E, 512, MIS, None) == 4
 
 
+def test_per_tensor_validation(L):
+    ts, qa, qw, gt = (L.ptpc_tensor_scale, L.ptpc_quant_act_static, L.ptpc_quant_weight_static,
+                      L.ptpc_gemm_tensor)
+    assert ts(A, 4, 256, 128, B, None) == 2                        # ld < C
+    assert ts(A, -1, 256, 256, B, None) == 2
+    assert ts(A, 4, 24, 24, B, None) == 3
+    assert ts(A, 4, 256, 256, NULL, None) == 1
+    assert ts(NULL, 4, 256, 256, B, None) == 1
+    assert ts(MIS, 4, 256, 256, B, None) == 4
+    assert ts(A, 4, 256, 260, B, None) == 4
+    assert qa(A, 0, 256, 256, B, C, 256, None) == 0                # empty: no-op
+    assert qa(A, 4, 256, 256, NULL, C, 256, None) == 1             # scale pointer
+    assert qa(A, 4, 256, 256, B, NULL, 256, None) == 1
+    assert qa(A, 4, 256, 256, B, C, 128, None) == 2
+    assert qa(A, 4, 24, 24, B, C, 32, None) == 3
+    assert qa(A, 4, 256, 256, MIS, C, 256, None) == 4
+    assert qw(A, 256, 0, 0, B, C, None) == 0
+    assert qw(A, 256, 512, 500, B, C, None) == 2
+    assert qw(A, 256, 520, 520, B, C, None) == 3
+    assert qw(A, 256, 512, 512, NULL, C, None) == 1
+    assert qw(A, 256, 512, 512, B, MIS, None) == 4
+    assert gt(A, 256, B, C, D, 0, 256, 512, E, 512, None) == 0
+    assert gt(A, 256, B, C, D, 4, 256, 500, E, 512, None) == 3
+    assert gt(A, 256, NULL, C, D, 4, 256, 512, E, 512, None) == 1
+    assert gt(A, 256, B, C, NULL, 4, 256, 512, E, 512, None) == 1
+    assert gt(A, 256, B, C, D, 4, 256, 512, E, 516, None) == 4
+
+
 def test_forced_launch_failure_reports_hip_error():
     """PTPC_FAULT=launch makes every launching call return PTPC_ERR_HIP from
     the host, without a GPU; checked in a child process so the setting does
@@ -134,9 +162,13 @@ r = [L.ptpc_quant_act(A, 4, 256, 256, B, 256, C, None),
      L.ptpc_unpack_weight(A, 256, 512, B, None),
      L.ptpc_gemm(A, 256, B, C, D, 4, 256, 512, E, 512, None),
      L.ptpc_gemm_unfused(A, 256, B, C, D, 4, 256, 512, E, 512, D, None),
+     L.ptpc_tensor_scale(A, 4, 256, 256, B, None),
+     L.ptpc_quant_act_static(A, 4, 256, 256, B, C, 256, None),
+     L.ptpc_quant_weight_static(A, 256, 512, 512, B, C, None),
+     L.ptpc_gemm_tensor(A, 256, B, C, D, 4, 256, 512, E, 512, None),
      L.ptpc_quant_act(A, 0, 256, 256, B, 256, C, None)]
 print(r)
-assert r == [5, 5, 5, 5, 5, 0], r
+assert r == [5, 5, 5, 5, 5, 5, 5, 5, 5, 0], r
 """ % ROOT
     env = dict(os.environ, PTPC_FAULT="launch", HIP_VISIBLE_DEVICES="")
     subprocess.run(["python", "-c", code], check=True, env=env)
