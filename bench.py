@@ -188,11 +188,17 @@ def sweep(args):
         out = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
         out2 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
         ws = torch.empty((T, Co), dtype=torch.float32, device=dev)
+        ws16 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
+        sx_t = sg.tensor_scale(x)
+        pw_t = sg.quant_weight_static(w, sg.tensor_scale(w))
         calls = {
             "quant_weight": lambda: sg.quant_weight(w, out=pw),
             "quant_act": lambda: sg.quant_act(x, qx=qx, dx=dx),
             "gemm_fused": lambda: sg.gemm(qx, dx, pw, out=out),
             "gemm_unfused": lambda: sg.gemm_unfused(qx, dx, pw, out=out2, workspace=ws),
+            "gemm_unfused_bf16": lambda: sg.gemm_unfused_bf16(qx, dx, pw, out=out2,
+                                                              workspace=ws16),
+            "gemm_tensor": lambda: sg.gemm_tensor(qx, sx_t, pw_t, out=out2),
         }
         ms = {}
         for k, fn in calls.items():
@@ -217,11 +223,13 @@ def sweep(args):
                                               / ms["gemm_fused"] / 1e6, 1),
             "gemm_unfused_tflops": round(flops / ms["gemm_unfused"] / 1e9, 1),
             "fused_over_unfused": round(ms["gemm_unfused"] / ms["gemm_fused"], 3),
+            "fused_over_unfused_bf16": round(ms["gemm_unfused_bf16"] / ms["gemm_fused"], 3),
+            "ptpc_over_per_tensor_gemm": round(ms["gemm_fused"] / ms["gemm_tensor"], 3),
             "quant_act_gbs": round(act_b / ms["quant_act"] / 1e6, 1),
             "quant_act_frac_hbm": round(act_b / ms["quant_act"] / 1e6 / PEAK_HBM_GBS, 4),
             "quant_weight_gbs": round((3.0 * Ci * Co + 4.0 * Co) / ms["quant_weight"] / 1e6, 1),
         }), flush=True)
-        del x, w, pw, qx, dx, out, out2, ws
+        del x, w, pw, qx, dx, out, out2, ws, ws16, sx_t, pw_t
         torch.cuda.empty_cache()
 
 
@@ -331,23 +339,26 @@ def main():
         sx_t = torch.empty((1,), dtype=torch.float32, device=dev)
         qx_t = torch.empty_like(qx)
         out_t = torch.empty_like(out)
+        ws16 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
         pt_calls = [("tensor_scale", lambda: sg.tensor_scale(x, d=sx_t)),
                     ("quant_act_static", lambda: sg.quant_act_static(x, sx_t, qx=qx_t)),
-                    ("gemm_tensor", lambda: sg.gemm_tensor(qx_t, sx_t, pw_t, out=out_t))]
+                    ("gemm_tensor", lambda: sg.gemm_tensor(qx_t, sx_t, pw_t, out=out_t)),
+                    ("gemm_unfused_bf16", lambda: sg.gemm_unfused_bf16(qx, dx, pw, out=out_t,
+                                                                       workspace=ws16))]
         for _ in range(3):
             for _, fn in pt_calls:
                 fn()
-        pt_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        pt_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(pt_calls) + 1)]
                  for _ in range(args.steps)]
         for k in range(args.steps):
             for i, (_, fn) in enumerate(pt_calls):
                 pt_ev[k][i].record(stream)
                 fn()
-            pt_ev[k][3].record(stream)
+            pt_ev[k][len(pt_calls)].record(stream)
         torch.cuda.synchronize()
         pt = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in pt_ev]))
               for i, (name, _) in enumerate(pt_calls)}
-        del sw_t, pw_t, sx_t, qx_t, out_t
+        del sw_t, pw_t, sx_t, qx_t, out_t, ws16
 
     # A plain device copy (torch copy_, 512 MiB read + 512 MiB written) as the
     # practical HBM ceiling next to the 8 TB/s peak.
@@ -433,6 +444,12 @@ def main():
         "cpu_baseline": None,
     }
     if pt is not None:
+        result["two_step_bf16"] = {
+            "what": "two-step form with a bf16 intermediate (GEMM -> bf16, then scale)",
+            "ms_avg": round(pt.pop("gemm_unfused_bf16"), 4),
+        }
+        result["two_step_bf16"]["fused_speedup"] = round(
+            result["two_step_bf16"]["ms_avg"] / avg["gemm_fused"], 4)
         result["per_tensor"] = {
             "what": "per-tensor FP8 comparator on the same inputs: tensor_scale(X) + "
                     "quant_act_static + gemm_tensor (weight quantized per tensor once)",

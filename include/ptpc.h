@@ -138,6 +138,23 @@ ptpc_status ptpc_gemm_unfused(const uint8_t* qx, int64_t ldq, const float* dx,
                               int64_t Ci, int64_t Co, void* out, int64_t ldo,
                               float* workspace, void* stream);
 
+/* Workspace needed by ptpc_gemm_unfused_bf16: 2 * T * Co bytes. */
+size_t ptpc_gemm_unfused_bf16_workspace_bytes(int64_t T, int64_t Co);
+
+/*
+ * The two-step form with a bf16 intermediate ([PTPC] §The challenge: two-step
+ * vs fused -- the listing leaves the intermediate's type open; this is its
+ * bf16 reading): step 1 writes ws = bf16(acc) unscaled ([T x Co], pitch Co,
+ * caller-allocated, ptpc_gemm_unfused_bf16_workspace_bytes(T, Co) bytes, 16-
+ * byte aligned), step 2 writes out = bf16((float(ws) * dx[t]) * dw[o]).
+ * Rounds twice, so it differs from ptpc_gemm in the last bf16 bit at times;
+ * it moves half the intermediate bytes of ptpc_gemm_unfused.
+ */
+ptpc_status ptpc_gemm_unfused_bf16(const uint8_t* qx, int64_t ldq, const float* dx,
+                                   const void* w_packed, const float* dw, int64_t T,
+                                   int64_t Ci, int64_t Co, void* out, int64_t ldo,
+                                   void* workspace, void* stream);
+
 /*
  * ---- Per-tensor ("standard") FP8, the comparator ------------------------
  * [PTPC] measures PTPC-FP8 against FP8 with one scale per tensor

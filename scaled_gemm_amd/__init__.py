@@ -26,7 +26,8 @@ _STATUS = {
 EXPORTS = (
     "ptpc_status_string", "ptpc_abi_version", "ptpc_quant_act", "ptpc_weight_packed_bytes",
     "ptpc_quant_weight", "ptpc_unpack_weight", "ptpc_gemm",
-    "ptpc_gemm_unfused_workspace_bytes", "ptpc_gemm_unfused", "ptpc_tensor_scale",
+    "ptpc_gemm_unfused_workspace_bytes", "ptpc_gemm_unfused",
+    "ptpc_gemm_unfused_bf16_workspace_bytes", "ptpc_gemm_unfused_bf16", "ptpc_tensor_scale",
     "ptpc_quant_act_static", "ptpc_quant_weight_static", "ptpc_gemm_tensor",
 )
 
@@ -66,6 +67,10 @@ def lib():
         L.ptpc_gemm_unfused_workspace_bytes.argtypes = [I, I]
         L.ptpc_gemm_unfused.restype = ctypes.c_int
         L.ptpc_gemm_unfused.argtypes = [P, I, P, P, P, I, I, I, P, I, P, P]
+        L.ptpc_gemm_unfused_bf16_workspace_bytes.restype = S
+        L.ptpc_gemm_unfused_bf16_workspace_bytes.argtypes = [I, I]
+        L.ptpc_gemm_unfused_bf16.restype = ctypes.c_int
+        L.ptpc_gemm_unfused_bf16.argtypes = [P, I, P, P, P, I, I, I, P, I, P, P]
         L.ptpc_tensor_scale.restype = ctypes.c_int
         L.ptpc_tensor_scale.argtypes = [P, I, I, I, P, P]
         L.ptpc_quant_act_static.restype = ctypes.c_int
@@ -175,6 +180,23 @@ def gemm_unfused(qx, dx, pw: PackedWeight, out=None, workspace=None, stream=None
     _check("ptpc_gemm_unfused",
            lib().ptpc_gemm_unfused(_ptr(qx), ldq, _ptr(dx), _ptr(pw.data), _ptr(pw.dw), T, Ci,
                                    pw.Co, _ptr(out), ldo, _ptr(workspace), _stream(stream)))
+    return out
+
+
+def gemm_unfused_bf16(qx, dx, pw: PackedWeight, out=None, workspace=None, stream=None):
+    """Two-step form with a bf16 intermediate: bf16(acc) to `workspace`, then scaled."""
+    T, Ci, ldq = _matrix(qx, torch.uint8, "qx")
+    if Ci != pw.Ci:
+        raise ValueError(f"qx has Ci={Ci}, weight has Ci={pw.Ci}")
+    if out is None:
+        out = torch.empty((T, pw.Co), dtype=torch.bfloat16, device=qx.device)
+    if workspace is None:
+        workspace = torch.empty((T, pw.Co), dtype=torch.bfloat16, device=qx.device)
+    _, _, ldo = _matrix(out, torch.bfloat16, "out")
+    _check("ptpc_gemm_unfused_bf16",
+           lib().ptpc_gemm_unfused_bf16(_ptr(qx), ldq, _ptr(dx), _ptr(pw.data), _ptr(pw.dw), T,
+                                        Ci, pw.Co, _ptr(out), ldo, _ptr(workspace),
+                                        _stream(stream)))
     return out
 
 

@@ -49,6 +49,19 @@ __device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 7; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Scales the fused epilogue applies: per token and per output column (the
+// method), one scalar each (the per-tensor comparator), or none (step 1 of
+// the bf16-intermediate two-step form: acc rounded to bf16 unscaled).
+constexpr int kTokenChannelScales = 0;
+constexpr int kTensorScales = 1;
+constexpr int kUnitScales = 2;
+
+__device__ __forceinline__ float4 scale_of_cols(const float* dw, int64_t col, int mode) {
+    if (mode == kTokenChannelScales) return *reinterpret_cast<const float4*>(dw + col);
+    const float v = (mode == kTensorScales) ? dw[0] : 1.0f;
+    return make_float4(v, v, v, v);
+}
+
 // Workgroup barrier without the release/acquire fences of __syncthreads():
 // the fence would wait for every load in flight into LDS (vmcnt 0), which
 // would drain the prefetch ring.  Callers wait for exactly the fills they
@@ -108,7 +121,7 @@ template <int BM, int BN, int WM, int WN, int NB, bool FUSED>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
     const uint8_t* __restrict__ wp, int64_t Kp, const float* __restrict__ dw,
-    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo, int tensor_scales) {
+    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo, int scale_mode) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MT = WTM / 32, NTL = WTN / 32;
@@ -333,7 +346,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             const int64_t row = m0 + wm * WTM + i * 32 + lr;
-            const float sx = (row < T) ? dx[tensor_scales ? 0 : row] : 0.0f;
+            const float sx =
+                (row < T) ? (scale_mode == kUnitScales ? 1.0f : dx[scale_mode ? 0 : row]) : 0.0f;
             const int sw_r = (lr / RB) % NC;
 #pragma unroll
             for (int j = 0; j < NTL; ++j) {
@@ -343,9 +357,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
                     if (row >= T || col >= Co) continue;  // Co % 16 == 0: runs are whole
                     const float a0 = acc[i][j][4 * g + 0], a1 = acc[i][j][4 * g + 1];
                     const float a2 = acc[i][j][4 * g + 2], a3 = acc[i][j][4 * g + 3];
-                    const float4 sw = tensor_scales
-                                          ? make_float4(dw[0], dw[0], dw[0], dw[0])
-                                          : *reinterpret_cast<const float4*>(dw + col);
+                    const float4 sw = scale_of_cols(dw, col, scale_mode);
                     uint2 pk;
                     pk.x = (uint32_t)f32_to_bf16_rne((a0 * sx) * sw.x) |
                            ((uint32_t)f32_to_bf16_rne((a1 * sx) * sw.y) << 16);
@@ -403,7 +415,7 @@ template <int MT, int NT, int NWAVE, int DEPTH, bool FUSED>
 __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
     const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
     const uint8_t* __restrict__ wp, int64_t Kp, const float* __restrict__ dw,
-    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo, int tensor_scales) {
+    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo, int scale_mode) {
     static_assert(NWAVE * NT * MT * 16 * 64 * 4 <= 160 * 1024, "partial sums exceed LDS");
     __shared__ float red[NWAVE][NT * MT][16][64];
     const int lane = threadIdx.x & 63;
@@ -519,9 +531,8 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
         const int64_t c = n0 + 32 * j + 8 * g + 4 * lg;
         if (row >= T || c >= Co) continue;
         if constexpr (FUSED) {
-            const float sx = dx[tensor_scales ? 0 : row];
-            const float4 sw = tensor_scales ? make_float4(dw[0], dw[0], dw[0], dw[0])
-                                            : *reinterpret_cast<const float4*>(dw + c);
+            const float sx = scale_mode == kUnitScales ? 1.0f : dx[scale_mode ? 0 : row];
+            const float4 sw = scale_of_cols(dw, c, scale_mode);
             uint2 pk;
             pk.x = (uint32_t)f32_to_bf16_rne((v[0] * sx) * sw.x) |
                    ((uint32_t)f32_to_bf16_rne((v[1] * sx) * sw.y) << 16);
@@ -538,13 +549,13 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
 template <int MT, int NT, int NWAVE, int DEPTH>
 static hipError_t launch_decode(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                                 const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
-                                int64_t ldo, float* fp32_out, hipStream_t s, int ts) {
+                                int64_t ldo, float* fp32_out, hipStream_t s, int mode) {
     const dim3 grid((unsigned)((Co + 32 * NT - 1) / (32 * NT)));
     const int64_t Kp = round_up_k(Ci);
     if (fp32_out == nullptr) {
         hipLaunchKernelGGL((gemm_decode_kernel<MT, NT, NWAVE, DEPTH, true>), grid,
                            dim3(NWAVE * 64), 0, s, qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out,
-                           ldo, ts);
+                           ldo, mode);
     } else {
         hipLaunchKernelGGL((gemm_decode_kernel<MT, NT, NWAVE, DEPTH, false>), grid,
                            dim3(NWAVE * 64), 0, s, qx, ldq, dx, wp, Kp, dw, T, Ci, Co,
@@ -577,15 +588,41 @@ __global__ __launch_bounds__(256) void rescale_kernel(const float* __restrict__ 
     }
 }
 
+// Step 2 of the bf16-intermediate two-step form: the unscaled result was
+// rounded to bf16 by step 1; scale it and round again.
+__global__ __launch_bounds__(256) void rescale_bf16_kernel(const uint16_t* __restrict__ ws,
+                                                           const float* __restrict__ dx,
+                                                           const float* __restrict__ dw,
+                                                           int64_t T, int64_t Co,
+                                                           uint16_t* __restrict__ out,
+                                                           int64_t ldo) {
+    const int64_t per_row = Co / 4;
+    const int64_t n = T * per_row;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = i / per_row;
+        const int64_t o = (i - t * per_row) * 4;
+        const uint2 a = *reinterpret_cast<const uint2*>(ws + t * Co + o);
+        const float4 sc = *reinterpret_cast<const float4*>(dw + o);
+        const float st = dx[t];
+        uint2 packed;
+        packed.x = (uint32_t)f32_to_bf16_rne((bf16lo_to_f32(a.x) * st) * sc.x) |
+                   ((uint32_t)f32_to_bf16_rne((bf16hi_to_f32(a.x) * st) * sc.y) << 16);
+        packed.y = (uint32_t)f32_to_bf16_rne((bf16lo_to_f32(a.y) * st) * sc.z) |
+                   ((uint32_t)f32_to_bf16_rne((bf16hi_to_f32(a.y) * st) * sc.w) << 16);
+        *reinterpret_cast<uint2*>(out + t * ldo + o) = packed;
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int NB>
 static hipError_t launch_tiles(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                                const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
-                               int64_t ldo, float* fp32_out, hipStream_t s, int ts) {
+                               int64_t ldo, float* fp32_out, hipStream_t s, int mode) {
     const dim3 grid((unsigned)(((Co + BN - 1) / BN) * ((T + BM - 1) / BM)));
     const int64_t Kp = round_up_k(Ci);
     if (fp32_out == nullptr) {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NB, true>), grid, dim3(WM * WN * 64), 0, s,
-                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out, ldo, ts);
+                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out, ldo, mode);
     } else {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NB, false>), grid, dim3(WM * WN * 64), 0, s,
                            qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)fp32_out, Co, 0);
@@ -593,10 +630,9 @@ static hipError_t launch_tiles(const uint8_t* qx, int64_t ldq, const float* dx, 
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
+static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                        const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
-                       int64_t ldo, float* fp32_out, hipStream_t s, bool per_tensor) {
-    const int ts = per_tensor ? 1 : 0;
+                       int64_t ldo, float* fp32_out, hipStream_t s, int ts) {
     // Tile choice: 256x256 keeps the most MFMA work per loaded byte; when it
     // leaves CUs idle or a badly filled last round, 256x128 (twice the tiles,
     // each costing about 0.6 of a 256x256 one) is taken if its rounds cost
@@ -629,12 +665,35 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
         e = launch_decode<1, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else
         e = launch_decode<1, 1, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    if (e != hipSuccess || fp32_out == nullptr) return e;
+    return e;
+}
+
+static int64_t rescale_blocks(int64_t T, int64_t Co) {
     const int64_t n = T * (Co / 4);
     int64_t blocks = (n + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(rescale_kernel, dim3((unsigned)blocks), dim3(256), 0, s, fp32_out, dx, dw,
-                       T, Co, out, ldo);
+    return blocks > 65536 ? 65536 : blocks;
+}
+
+hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
+                       const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
+                       int64_t ldo, float* fp32_out, hipStream_t s, bool per_tensor) {
+    const hipError_t e = launch_main(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s,
+                                     per_tensor ? kTensorScales : kTokenChannelScales);
+    if (e != hipSuccess || fp32_out == nullptr) return e;
+    hipLaunchKernelGGL(rescale_kernel, dim3((unsigned)rescale_blocks(T, Co)), dim3(256), 0, s,
+                       fp32_out, dx, dw, T, Co, out, ldo);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_unfused_bf16(const uint8_t* qx, int64_t ldq, const float* dx,
+                                    const uint8_t* wp, const float* dw, int64_t T, int64_t Ci,
+                                    int64_t Co, uint16_t* out, int64_t ldo, uint16_t* ws,
+                                    hipStream_t s) {
+    const hipError_t e =
+        launch_main(qx, ldq, dx, wp, dw, T, Ci, Co, ws, Co, nullptr, s, kUnitScales);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(rescale_bf16_kernel, dim3((unsigned)rescale_blocks(T, Co)), dim3(256), 0,
+                       s, ws, dx, dw, T, Co, out, ldo);
     return hipGetLastError();
 }
 

@@ -38,4 +38,11 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
                        const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                        int64_t ldo, float* fp32_out, hipStream_t s, bool per_tensor = false);
 
+// The bf16-intermediate two-step form: step 1 writes bf16(acc) unscaled to
+// ws ([T x Co], pitch Co), step 2 scales it into bf16 `out`.
+hipError_t launch_gemm_unfused_bf16(const uint8_t* qx, int64_t ldq, const float* dx,
+                                    const uint8_t* wp, const float* dw, int64_t T, int64_t Ci,
+                                    int64_t Co, uint16_t* out, int64_t ldo, uint16_t* ws,
+                                    hipStream_t s);
+
 }  // namespace ptpc

@@ -140,6 +140,25 @@ ptpc_status ptpc_gemm_unfused(const uint8_t* qx, int64_t ldq, const float* dx,
                                       as_stream(stream)));
 }
 
+size_t ptpc_gemm_unfused_bf16_workspace_bytes(int64_t T, int64_t Co) {
+    if (T <= 0 || Co <= 0) return 0;
+    return (size_t)T * (size_t)Co * 2;
+}
+
+ptpc_status ptpc_gemm_unfused_bf16(const uint8_t* qx, int64_t ldq, const float* dx,
+                                   const void* w_packed, const float* dw, int64_t T, int64_t Ci,
+                                   int64_t Co, void* out, int64_t ldo, void* workspace,
+                                   void* stream) {
+    ptpc_status st = check_gemm(qx, ldq, dx, w_packed, dw, T, Ci, Co, out, ldo);
+    if (st != PTPC_OK || T == 0 || Co == 0) return st;
+    if (workspace == nullptr) return PTPC_ERR_NULL;
+    if (!aligned16(workspace)) return PTPC_ERR_ALIGN;
+    if (forced_launch_failure()) return PTPC_ERR_HIP;
+    return from_hip(ptpc::launch_gemm_unfused_bf16(
+        qx, ldq, dx, static_cast<const uint8_t*>(w_packed), dw, T, Ci, Co,
+        static_cast<uint16_t*>(out), ldo, static_cast<uint16_t*>(workspace), as_stream(stream)));
+}
+
 // ---- per-tensor comparator ---------------------------------------------
 
 ptpc_status ptpc_tensor_scale(const void* x, int64_t R, int64_t C, int64_t ld, float* d,

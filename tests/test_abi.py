@@ -116,6 +116,10 @@ def test_gemm_validation(L):
         assert f(A, (1 << 22) + 16, B, C, D, 4, 256, 512, E, 512) == 3
         assert f(A, (1 << 22) + 16, B, C, D, 4, (1 << 22) + 16, 512, E, 512) == 3
     assert L.ptpc_gemm_unfused(A, 256, B, C, D, 4, 256, 512, E, 512, NULL, None) == 1
+    assert L.ptpc_gemm_unfused_bf16(A, 256, B, C, D, 4, 256, 512, E, 512, NULL, None) == 1
+    assert L.ptpc_gemm_unfused_bf16(A, 256, B, C, D, 4, 256, 512, E, 512, MIS, None) == 4
+    assert L.ptpc_gemm_unfused_bf16(A, 256, B, C, D, 4, 256, 500, E, 512, D, None) == 3
+    assert L.ptpc_gemm_unfused_bf16_workspace_bytes(3, 16) == 3 * 16 * 2
     assert L.ptpc_gemm_unfused(A, 256, B, C, D, 4, 256, 512, E, 512, MIS, None) == 4
 
 
@@ -166,9 +170,10 @@ r = [L.ptpc_quant_act(A, 4, 256, 256, B, 256, C, None),
      L.ptpc_quant_act_static(A, 4, 256, 256, B, C, 256, None),
      L.ptpc_quant_weight_static(A, 256, 512, 512, B, C, None),
      L.ptpc_gemm_tensor(A, 256, B, C, D, 4, 256, 512, E, 512, None),
+     L.ptpc_gemm_unfused_bf16(A, 256, B, C, D, 4, 256, 512, E, 512, D, None),
      L.ptpc_quant_act(A, 0, 256, 256, B, 256, C, None)]
 print(r)
-assert r == [5, 5, 5, 5, 5, 5, 5, 5, 5, 0], r
+assert r == [5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 0], r
 """ % ROOT
     env = dict(os.environ, PTPC_FAULT="launch", HIP_VISIBLE_DEVICES="")
     subprocess.run(["python", "-c", code], check=True, env=env)

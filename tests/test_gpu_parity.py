@@ -47,11 +47,30 @@ def run_path(x_bits, w_bits):
     pw = sg.quant_weight(w)
     out = sg.gemm(qx, dx, pw)
     out2 = sg.gemm_unfused(qx, dx, pw)
+    ws3 = torch.empty_like(out)
+    out3 = sg.gemm_unfused_bf16(qx, dx, pw, workspace=ws3)
     qw = sg.unpack_weight(pw)
     torch.cuda.synchronize()
     return dict(qx=qx.cpu().numpy(), dx=dx.cpu().numpy(), qw=qw.cpu().numpy(),
                 dw=pw.dw.cpu().numpy(), out=dev_to_bits(out), out2=dev_to_bits(out2),
-                packed=pw.data.cpu().numpy())
+                out3=dev_to_bits(out3), ws3=dev_to_bits(ws3), packed=pw.data.cpu().numpy())
+
+
+def check_bf16_two_step(g, ref, what, rows=None, cols=None):
+    """The bf16-intermediate two-step form: within the bar of the exact
+    reference, and its step 2 is exactly bf16((ws * dx[t]) * dw[o]) in fp32."""
+    out3, ws3 = g["out3"], g["ws3"]
+    T, Co = ws3.shape
+    if rows is None:
+        check_close(out3, ref, f"{what} bf16 two-step")
+        w32 = workloads.bf16_bits_to_f32(ws3)
+        want = workloads.f32_to_bf16_bits((w32 * g["dx"][:, None]) * g["dw"][None, :])
+        assert np.array_equal(out3, want), f"{what}: bf16 two-step step 2"
+    else:
+        check_close(out3[rows, cols], ref, f"{what} bf16 two-step (sampled)")
+        w32 = workloads.bf16_bits_to_f32(ws3[rows, cols])
+        want = workloads.f32_to_bf16_bits((w32 * g["dx"][rows]) * g["dw"][cols])
+        assert np.array_equal(out3[rows, cols], want), f"{what}: bf16 two-step step 2"
 
 
 def check_quant(g, x_bits, w_bits, what):
@@ -114,6 +133,7 @@ def test_full_parity(name, T, Ci, Co):
     ref = oracle.apply_scales(oracle.gemm_exact(qx, qw), dx, dw)
     check_close(g["out"], ref, f"{name} fused")
     assert np.array_equal(g["out"], g["out2"]), "fused and two-step differ"
+    check_bf16_two_step(g, ref, name)
 
 
 # ---------------------------------------------------------------------------
@@ -128,6 +148,7 @@ def sampled_case(x, w, what, seed):
     out = g["out"].reshape(T, Co)
     check_close(out[rows, cols], ref, f"{what} fused (sampled)")
     assert np.array_equal(g["out"], g["out2"]), f"{what}: fused and two-step differ"
+    check_bf16_two_step(g, ref, what, rows, cols)
     return g
 
 
