@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="run a plain device copy of this many MiB (3x) before timing, "
                         "as the reference kernel for HBM byte counters")
+    p.add_argument("--model-load", action="store_true",
+                   help="quantize + prepack every linear weight of the 80 Llama-3.1-70B "
+                        "decoder layers and report the load-time cost (one JSON line)")
     p.add_argument("--sweep", action="store_true",
                    help="one JSON line per workload shape (every config, every 70B layer x T): "
                         "quant_act GB/s, fused / two-step GEMM TFLOP/s; not the bench line")
@@ -158,6 +161,56 @@ def cpu_baseline(x_bits, w_bits, target_s):
                        f"(weight quantization {t_w:.1f} s); {nthr} OpenMP threads")}
 
 
+def model_load(args):
+    """Load-time weight quantization at model scale: each of the 80 decoder
+    layers' four linear weights is drawn in bf16 on the GPU, quantized per
+    output channel and prepacked (HIP events around each ptpc_quant_weight),
+    and the bf16 copy is freed, as a loader that quantizes on the fly would;
+    the packed weights of all layers stay resident."""
+    import numpy as np
+    import torch
+
+    import scaled_gemm_amd as sg
+    import workloads
+
+    dev = torch.device("cuda:0")
+    sg.lib()
+    stream = torch.cuda.current_stream()
+    packed, times, elems = [], [], 0
+    t0 = time.perf_counter()
+    for layer in range(workloads.LLAMA70B_LAYERS):
+        for index, (name, (Ci, Co)) in enumerate(workloads.SWEEP_LAYERS.items()):
+            w = workloads.device_weight(layer, index, Ci, Co, 0.01, dev)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pw = sg.quant_weight(w)
+            e1.record(stream)
+            packed.append(pw)
+            times.append((e0, e1))
+            elems += Ci * Co
+            del w
+        if layer % 10 == 9:
+            torch.cuda.synchronize()
+            print(f"# layers done: {layer + 1}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in times]
+    total_ms = float(np.sum(ms))
+    resident = sum(p.data.numel() + 4 * p.dw.numel() for p in packed)
+    print(json.dumps({
+        "what": "load-time per-channel quantization + prepack of every linear weight of "
+                "Llama-3.1-70B (80 layers x qkv/o/gate_up/down), bf16 drawn on the GPU",
+        "layers": workloads.LLAMA70B_LAYERS, "weights": len(packed),
+        "bf16_bytes": 2 * elems, "packed_bytes_resident": resident,
+        "quant_weight_ms_total": round(total_ms, 2),
+        "quant_weight_gbs": round(3.0 * elems / (total_ms * 1e-3) / 1e9, 1),
+        "per_layer_ms": round(total_ms / workloads.LLAMA70B_LAYERS, 3),
+        "max_memory_allocated_gb": round(torch.cuda.max_memory_allocated() / 1e9, 1),
+        "wall_s_including_generation": round(wall, 1),
+    }), flush=True)
+
+
 def sweep(args):
     """Per-shape kernel rates over every workload shape (HIP events around each
     launch on the launch stream, after a warm-up)."""
@@ -237,6 +290,9 @@ def main():
     args = parse()
     if args.sweep:
         sweep(args)
+        return
+    if args.model_load:
+        model_load(args)
         return
     if args.traffic_from:
         rec = traffic_record(args.traffic_from[0], args.traffic_from[1], args.workload,

@@ -31,6 +31,11 @@ scaled in float32, then rounded to bf16 with round-to-nearest-even):
                 to a value drawn from U[500, 5e4] (sign drawn); for T = 1 the
                 single row gets that planted entry.  W ~ N(0, 0.01^2) per layer.
 
+  70b model load  (timing only, no oracle side) every linear weight of the
+                80 decoder layers, qkv / o / gate_up / down shapes as above,
+                W ~ N(0, 0.01^2) drawn in bf16 on the GPU by torch's seeded
+                Philox generator (seed = 1000 * layer + index).
+
 Draw order per call: X base, outlier channels, outlier factors, special
 rows, then W from its own stream.  X and W use separate generators
 (``default_rng([seed, tag, ...])``) so a layer's W is the same for every T.
@@ -176,3 +181,17 @@ def make(name: str, seed: int = 0, T: int = None, layer: str = None):
 def random_bf16(rng, rows, cols, sigma=1.0):
     """Plain N(0, sigma^2) bf16 matrix (for ad-hoc shapes in tests)."""
     return _normal_bf16(rng, rows, cols, sigma)
+
+
+LLAMA70B_LAYERS = 80
+
+
+def device_weight(layer: int, index: int, Ci: int, Co: int, sigma: float, device):
+    """One synthetic bf16 weight [Ci x Co] drawn directly on `device` (torch's
+    seeded Philox generator), for load-time measurements at model scale where
+    host generation and transfer of ~140 GB would dominate."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(1000 * layer + index)
+    return torch.empty((Ci, Co), device=device, dtype=torch.bfloat16).normal_(0.0, sigma,
+                                                                             generator=g)
