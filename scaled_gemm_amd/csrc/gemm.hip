@@ -341,8 +341,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
         constexpr int NC = WTN / 8;                  // 16-byte chunks per row
         constexpr int RB = 256 / P;
         constexpr int RPI = 64 / NC;                 // rows per read instruction
-        static_assert(NW * 32 * P <= A_SLOT && RB >= 1 && RPI >= 1, "staging");
-        uint8_t* const stage = a_s0 + wave * (32 * P);
+        // Wave regions of 32*P bytes, as many per A slot as fit, slots in
+        // order (all three A slots are idle after the loop).
+        constexpr int RPS = A_SLOT / (32 * P);       // regions per A slot
+        static_assert(RPS >= 1 && NW <= 3 * RPS && RB >= 1 && RPI >= 1, "staging");
+        const int sl = wave / RPS;
+        uint8_t* const stage =
+            (sl == 0 ? a_s0 : sl == 1 ? a_s1 : a_s2) + (wave - sl * RPS) * (32 * P);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             const int64_t row = m0 + wm * WTM + i * 32 + lr;
@@ -630,16 +635,26 @@ static hipError_t launch_tiles(const uint8_t* qx, int64_t ldq, const float* dx, 
     return hipGetLastError();
 }
 
+#ifndef TILE_COST_256x128
+#define TILE_COST_256x128 0.69
+#endif
+#ifndef TILE_COST_192x256
+#define TILE_COST_192x256 0.88
+#endif
 static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                        const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                        int64_t ldo, float* fp32_out, hipStream_t s, int ts) {
     // Tile choice: 256x256 keeps the most MFMA work per loaded byte; when it
-    // leaves CUs idle or a badly filled last round, 256x128 (twice the tiles,
-    // each costing about 0.6 of a 256x256 one) is taken if its rounds cost
-    // less.
+    // leaves CUs idle or a badly filled last round, 192x256 or 256x128 (more
+    // tiles, each costing 0.88 or 0.69 of a 256x256 one, measured on the
+    // 1024-token 70B layers) is taken if its rounds cost less.
     auto rounds = [](int64_t tiles) { return (tiles + kCus - 1) / kCus; };
-    const int64_t t256 = ((T + 255) / 256) * ((Co + 255) / 256);
-    const int64_t t128 = ((T + 255) / 256) * ((Co + 127) / 128);
+    auto tiles = [&](int64_t bm, int64_t bn) { return ((T + bm - 1) / bm) * ((Co + bn - 1) / bn); };
+    // Cost in 256x256 tile-times of each tiled form: rounds of 256 CUs times
+    // the measured time of one tile relative to a 256x256 one.
+    const double c256 = (double)rounds(tiles(256, 256));
+    const double c128 = TILE_COST_256x128 * (double)rounds(tiles(256, 128));
+    const double c192 = TILE_COST_192x256 * (double)rounds(tiles(192, 256));
     // Up to 64 tokens the weight stream decides.  The tiled kernel reads
     // each weight byte once per row tile and keeps the activation in LDS, but
     // with few column tiles it leaves CUs idle; the few-token kernel splits K
@@ -649,8 +664,10 @@ static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, c
     // form (half the activation re-reads) pays off from 16 tokens on, once
     // the 32-column grid no longer fits the CUs in one round.
     hipError_t e;
-    if (T >= 256 && 3 * rounds(t128) < 5 * rounds(t256))
+    if (T >= 256 && c128 < c256 && c128 <= c192)
         e = launch_tiles<256, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+    else if (T >= 256 && c192 < c256)
+        e = launch_tiles<192, 256, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T >= 256)
         e = launch_tiles<256, 256, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T > 64 || (T > 32 && (Co + 127) / 128 >= kCus))

@@ -110,6 +110,7 @@ FULL_CASES = [
     ("ragged", 24, 208, 8208),
     ("ragged", 600, 256, 2048),
     ("ragged", 513, 512, 2064),
+    ("ragged", 600, 144, 22000),
 ]
 
 
