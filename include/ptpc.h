@@ -122,6 +122,29 @@ ptpc_status ptpc_gemm(const uint8_t* qx, int64_t ldq, const float* dx,
                       int64_t Ci, int64_t Co, void* out, int64_t ldo,
                       void* stream);
 
+/*
+ * Workspace that lets ptpc_gemm_ws split K across workgroups: nonzero only
+ * for token counts whose output tiles are too few to occupy the GPU (65..255
+ * tokens with few output columns), then 4 * S * T * Co bytes for S K ranges.
+ */
+size_t ptpc_gemm_workspace_bytes(int64_t T, int64_t Ci, int64_t Co);
+
+/*
+ * ptpc_gemm with a caller-provided workspace (ptpc_gemm_workspace_bytes(T,
+ * Ci, Co) bytes, 16-byte aligned, contents ignored and overwritten).  Where
+ * that size is 0 this is exactly ptpc_gemm (workspace may be NULL).
+ * Otherwise K is cut into S ranges, each workgroup writes the fp32 partial
+ * sums of one range of one output tile to the workspace, and one more pass
+ * adds the S partials in range order and applies the same epilogue
+ * bf16((sum * dx[t]) * dw[o]).  The result is deterministic; it can differ
+ * from ptpc_gemm's in the last bf16 bit (another fp32 summation order).
+ * PTPC_ERR_NULL for a missing, PTPC_ERR_SHAPE for a too small workspace.
+ */
+ptpc_status ptpc_gemm_ws(const uint8_t* qx, int64_t ldq, const float* dx,
+                         const void* w_packed, const float* dw, int64_t T,
+                         int64_t Ci, int64_t Co, void* out, int64_t ldo,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace needed by ptpc_gemm_unfused: 4 * T * Co bytes (fp32 [T x Co]). */
 size_t ptpc_gemm_unfused_workspace_bytes(int64_t T, int64_t Co);
 

@@ -26,6 +26,7 @@ _STATUS = {
 EXPORTS = (
     "ptpc_status_string", "ptpc_abi_version", "ptpc_quant_act", "ptpc_weight_packed_bytes",
     "ptpc_quant_weight", "ptpc_unpack_weight", "ptpc_gemm",
+    "ptpc_gemm_workspace_bytes", "ptpc_gemm_ws",
     "ptpc_gemm_unfused_workspace_bytes", "ptpc_gemm_unfused",
     "ptpc_gemm_unfused_bf16_workspace_bytes", "ptpc_gemm_unfused_bf16", "ptpc_tensor_scale",
     "ptpc_quant_act_static", "ptpc_quant_weight_static", "ptpc_gemm_tensor",
@@ -67,6 +68,10 @@ def lib():
         L.ptpc_gemm_unfused_workspace_bytes.argtypes = [I, I]
         L.ptpc_gemm_unfused.restype = ctypes.c_int
         L.ptpc_gemm_unfused.argtypes = [P, I, P, P, P, I, I, I, P, I, P, P]
+        L.ptpc_gemm_workspace_bytes.restype = S
+        L.ptpc_gemm_workspace_bytes.argtypes = [I, I, I]
+        L.ptpc_gemm_ws.restype = ctypes.c_int
+        L.ptpc_gemm_ws.argtypes = [P, I, P, P, P, I, I, I, P, I, P, S, P]
         L.ptpc_gemm_unfused_bf16_workspace_bytes.restype = S
         L.ptpc_gemm_unfused_bf16_workspace_bytes.argtypes = [I, I]
         L.ptpc_gemm_unfused_bf16.restype = ctypes.c_int
@@ -164,6 +169,30 @@ def gemm(qx, dx, pw: PackedWeight, out=None, stream=None):
     _, _, ldo = _matrix(out, torch.bfloat16, "out")
     _check("ptpc_gemm", lib().ptpc_gemm(_ptr(qx), ldq, _ptr(dx), _ptr(pw.data), _ptr(pw.dw), T,
                                         Ci, pw.Co, _ptr(out), ldo, _stream(stream)))
+    return out
+
+
+def gemm_workspace_bytes(T: int, Ci: int, Co: int) -> int:
+    return int(lib().ptpc_gemm_workspace_bytes(T, Ci, Co))
+
+
+def gemm_ws(qx, dx, pw: PackedWeight, out=None, workspace=None, stream=None):
+    """ptpc_gemm_ws: the fused GEMM, splitting K across workgroups where the
+    output tiles alone leave the GPU idle (workspace: uint8 tensor of at least
+    gemm_workspace_bytes(T, Ci, Co) bytes; allocated here if not given)."""
+    T, Ci, ldq = _matrix(qx, torch.uint8, "qx")
+    if Ci != pw.Ci:
+        raise ValueError(f"qx has Ci={Ci}, weight has Ci={pw.Ci}")
+    if out is None:
+        out = torch.empty((T, pw.Co), dtype=torch.bfloat16, device=qx.device)
+    need = gemm_workspace_bytes(T, Ci, pw.Co)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=qx.device)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _, _, ldo = _matrix(out, torch.bfloat16, "out")
+    _check("ptpc_gemm_ws", lib().ptpc_gemm_ws(_ptr(qx), ldq, _ptr(dx), _ptr(pw.data), _ptr(pw.dw),
+                                              T, Ci, pw.Co, _ptr(out), ldo, _ptr(workspace),
+                                              nbytes, _stream(stream)))
     return out
 
 

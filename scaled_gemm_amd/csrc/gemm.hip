@@ -88,9 +88,8 @@ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 constexpr int kXcds = 8;
 constexpr int64_t kCus = 256;
 constexpr int kGroupN = 8;
-__device__ __forceinline__ void tile_of(int gm, int gn, int& tm, int& tn) {
+__device__ __forceinline__ void tile_of(int i, int gm, int gn, int& tm, int& tn) {
     const int n = gm * gn;
-    int i = blockIdx.x;
     if (n % kXcds == 0) i = (i % kXcds) * (n / kXcds) + i / kXcds;
     const int group = i / (kGroupN * gm);
     const int first_n = group * kGroupN;
@@ -121,7 +120,8 @@ template <int BM, int BN, int WM, int WN, int NB, bool FUSED>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
     const uint8_t* __restrict__ wp, int64_t Kp, const float* __restrict__ dw,
-    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo, int scale_mode) {
+    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo, int scale_mode,
+    int splits) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MT = WTM / 32, NTL = WTN / 32;
@@ -152,18 +152,31 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
+    // Split K (splits > 1, two-step form only): workgroup b takes K range
+    // b / ntiles of tile b % ntiles and writes its partial sums to slice
+    // b / ntiles of the fp32 output.  Ranges are whole A pairs (even steps).
+    const int gm = (int)((T + BM - 1) / BM), gn = (int)((Co + BN - 1) / BN);
+    const int ntiles = gm * gn;
+    const int split = (int)blockIdx.x / ntiles;
     int tm, tn;
-    tile_of((int)((T + BM - 1) / BM), (int)((Co + BN - 1) / BN), tm, tn);
+    tile_of((int)blockIdx.x - split * ntiles, gm, gn, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
-    const int nks = (int)(Kp / BK);                  // K steps with data (even)
+    const int nks = (int)(Kp / BK);                  // K steps of the packed weight (even)
+    const int per = ((nks + splits - 1) / splits + 1) & ~1;
+    const int ks0 = split * per < nks ? split * per : nks;
+    const int nsteps = (ks0 + per < nks ? ks0 + per : nks) - ks0;
+    const int64_t k_end = (int64_t)(ks0 + nsteps) * BK < Ci ? (int64_t)(ks0 + nsteps) * BK : Ci;
 
-    // Buffer descriptors based at this tile's first row; rows past the end
-    // and K past the data land beyond num_records and read as zero.
+    // Buffer descriptors based at this tile's first row and this split's
+    // first K step; rows past the end and K past the range land beyond
+    // num_records or are sent there, and read as zero.
     const int64_t a_rows = (T - m0 < BM) ? (T - m0) : BM;
     const int64_t b_rows = (Co - n0 < BN) ? (Co - n0) : BN;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(qx + m0 * ldq, (uint32_t)(a_rows * ldq));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(wp + n0 * Kp, (uint32_t)(b_rows * Kp));
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(qx + m0 * ldq + (int64_t)ks0 * BK, (uint32_t)(a_rows * ldq));
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(wp + n0 * Kp + (int64_t)ks0 * 1024, (uint32_t)(b_rows * Kp));
 
     // A pair load: lane L owns LDS row L/8 of its 8-row block, slot L%8, and
     // fetches the logical chunk that belongs in that slot.
@@ -193,7 +206,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
         const int k0 = q * 2 * BK;
 #pragma unroll
         for (int p = 0; p < A_HALF_PER_W; ++p) {
-            const bool kin = (int64_t)(k0 + a_chunk[h][p] * 16) < Ci;
+            const bool kin = (int64_t)ks0 * BK + k0 + a_chunk[h][p] * 16 < k_end;
             const uint32_t off = (a_off[h][p] != kOutOfRange && kin) ? a_off[h][p] + k0
                                                                      : kOutOfRange;
             const int blk = h * (A_BLK / 2) + wave + p * NW;
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     };
     // Loads of B for step ks.
     auto issue_b = [&](int ks, uint8_t* slot) {
-        const bool kin = ks < nks;
+        const bool kin = ks < nsteps;
 #pragma unroll
         for (int p = 0; p < B_PER_W; ++p) {
             const uint32_t off =
@@ -304,7 +317,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     // extra zero steps are multiplied).  Unrolled by the period so that every
     // slot and fragment set is named statically.
     constexpr int P = 6 * NB / gcd_c(6, NB);
-    if (nks > 0) {
+    if (nsteps > 0) {
         // Fills as if issued at the tops of steps -NB .. -1.
         issue_a_half(0, 0, a_slots[0]);
         issue_a_half(0, 1, a_slots[0]);
@@ -316,7 +329,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
         wait_counts<0, 0>();
         lds_barrier();
         read_frags(a_slots[0], 0, b_slots[0], fr_a[0], fr_b[0]);
-        for (int s0 = 0; s0 < nks; s0 += P) {
+        for (int s0 = 0; s0 < nsteps; s0 += P) {
             [&]<int... Us>(std::integer_sequence<int, Us...>) {
                 ((top(), step(std::integral_constant<int, Us>{}, s0 + Us)), ...);
             }(std::make_integer_sequence<int, P>{});
@@ -398,7 +411,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
                 for (int g = 0; g < 4; ++g) {
                     const int64_t col = n0 + wn * WTN + j * 32 + 8 * g + 4 * lg;
                     if (col >= Co) continue;
-                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * Co + col) =
+                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) +
+                                               (int64_t)split * T * Co + row * Co + col) =
                         make_float4(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
                                     acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
                 }
@@ -619,18 +633,54 @@ __global__ __launch_bounds__(256) void rescale_bf16_kernel(const uint16_t* __res
     }
 }
 
+// Split-K epilogue: the partial sums of the S K ranges, added in range order
+// (so the result does not depend on timing), then scaled and rounded once.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws,
+                                                            int splits,
+                                                            const float* __restrict__ dx,
+                                                            const float* __restrict__ dw,
+                                                            int64_t T, int64_t Co,
+                                                            uint16_t* __restrict__ out,
+                                                            int64_t ldo) {
+    const int64_t per_row = Co / 4;
+    const int64_t n = T * per_row;
+    const int64_t slice = T * Co;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = i / per_row;
+        const int64_t o = (i - t * per_row) * 4;
+        float4 a = *reinterpret_cast<const float4*>(ws + t * Co + o);
+        for (int k = 1; k < splits; ++k) {
+            const float4 b = *reinterpret_cast<const float4*>(ws + k * slice + t * Co + o);
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        const float4 sc = *reinterpret_cast<const float4*>(dw + o);
+        const float st = dx[t];
+        uint2 packed;
+        packed.x = (uint32_t)f32_to_bf16_rne((a.x * st) * sc.x) |
+                   ((uint32_t)f32_to_bf16_rne((a.y * st) * sc.y) << 16);
+        packed.y = (uint32_t)f32_to_bf16_rne((a.z * st) * sc.z) |
+                   ((uint32_t)f32_to_bf16_rne((a.w * st) * sc.w) << 16);
+        *reinterpret_cast<uint2*>(out + t * ldo + o) = packed;
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int NB>
 static hipError_t launch_tiles(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                                const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
-                               int64_t ldo, float* fp32_out, hipStream_t s, int mode) {
-    const dim3 grid((unsigned)(((Co + BN - 1) / BN) * ((T + BM - 1) / BM)));
+                               int64_t ldo, float* fp32_out, hipStream_t s, int mode,
+                               int splits = 1) {
+    const dim3 grid((unsigned)(((Co + BN - 1) / BN) * ((T + BM - 1) / BM) * splits));
     const int64_t Kp = round_up_k(Ci);
     if (fp32_out == nullptr) {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NB, true>), grid, dim3(WM * WN * 64), 0, s,
-                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out, ldo, mode);
+                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out, ldo, mode, 1);
     } else {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NB, false>), grid, dim3(WM * WN * 64), 0, s,
-                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)fp32_out, Co, 0);
+                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)fp32_out, Co, 0, splits);
     }
     return hipGetLastError();
 }
@@ -699,6 +749,30 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
     if (e != hipSuccess || fp32_out == nullptr) return e;
     hipLaunchKernelGGL(rescale_kernel, dim3((unsigned)rescale_blocks(T, Co)), dim3(256), 0, s,
                        fp32_out, dx, dw, T, Co, out, ldo);
+    return hipGetLastError();
+}
+
+// Split-K plan for shapes whose tiled grid leaves most CUs idle: 65..255
+// tokens on 128x128 tiles, K cut into S ranges of at least 16 steps so that
+// tiles x S fills the CUs.  Returns S (1: no split).
+int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co) {
+    if (T <= 64 || T >= 256) return 1;
+    const int64_t tiles = ((T + 127) / 128) * ((Co + 127) / 128);
+    int64_t S = kCus / tiles;
+    const int64_t nks = round_up_k(Ci) / BK;
+    if (S > nks / 16) S = nks / 16;
+    if (S > 8) S = 8;
+    return S < 2 ? 1 : (int)S;
+}
+
+hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
+                              const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
+                              int64_t ldo, float* ws, int splits, hipStream_t s) {
+    const hipError_t e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo,
+                                                          ws, s, kTokenChannelScales, splits);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)rescale_blocks(T, Co)), dim3(256), 0,
+                       s, ws, splits, dx, dw, T, Co, out, ldo);
     return hipGetLastError();
 }
 

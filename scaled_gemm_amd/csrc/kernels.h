@@ -45,4 +45,13 @@ hipError_t launch_gemm_unfused_bf16(const uint8_t* qx, int64_t ldq, const float*
                                     int64_t Co, uint16_t* out, int64_t ldo, uint16_t* ws,
                                     hipStream_t s);
 
+// Split-K for token counts whose tiled grid leaves most CUs idle: the number
+// of K ranges (1 = no split; then the call is ptpc_gemm's), and the launch
+// writing S fp32 partial slices [S][T][Co] to ws before one reduce + scale
+// pass into bf16 `out`.
+int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co);
+hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
+                              const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
+                              int64_t ldo, float* ws, int splits, hipStream_t s);
+
 }  // namespace ptpc

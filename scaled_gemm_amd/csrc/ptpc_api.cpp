@@ -140,6 +140,34 @@ ptpc_status ptpc_gemm_unfused(const uint8_t* qx, int64_t ldq, const float* dx,
                                       as_stream(stream)));
 }
 
+size_t ptpc_gemm_workspace_bytes(int64_t T, int64_t Ci, int64_t Co) {
+    if (T <= 0 || Ci <= 0 || Co <= 0 || Ci % 16 != 0 || Co % 16 != 0) return 0;
+    const int S = ptpc::gemm_splitk_plan(T, Ci, Co);
+    return S > 1 ? (size_t)S * (size_t)T * (size_t)Co * sizeof(float) : 0;
+}
+
+ptpc_status ptpc_gemm_ws(const uint8_t* qx, int64_t ldq, const float* dx, const void* w_packed,
+                         const float* dw, int64_t T, int64_t Ci, int64_t Co, void* out,
+                         int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
+    ptpc_status st = check_gemm(qx, ldq, dx, w_packed, dw, T, Ci, Co, out, ldo);
+    if (st != PTPC_OK || T == 0 || Co == 0) return st;
+    const size_t need = ptpc_gemm_workspace_bytes(T, Ci, Co);
+    if (need > 0) {
+        if (workspace == nullptr) return PTPC_ERR_NULL;
+        if (workspace_bytes < need) return PTPC_ERR_SHAPE;
+        if (!aligned16(workspace)) return PTPC_ERR_ALIGN;
+    }
+    if (forced_launch_failure()) return PTPC_ERR_HIP;
+    if (need == 0)
+        return from_hip(ptpc::launch_gemm(qx, ldq, dx, static_cast<const uint8_t*>(w_packed), dw,
+                                          T, Ci, Co, static_cast<uint16_t*>(out), ldo, nullptr,
+                                          as_stream(stream)));
+    return from_hip(ptpc::launch_gemm_splitk(
+        qx, ldq, dx, static_cast<const uint8_t*>(w_packed), dw, T, Ci, Co,
+        static_cast<uint16_t*>(out), ldo, static_cast<float*>(workspace),
+        ptpc::gemm_splitk_plan(T, Ci, Co), as_stream(stream)));
+}
+
 size_t ptpc_gemm_unfused_bf16_workspace_bytes(int64_t T, int64_t Co) {
     if (T <= 0 || Co <= 0) return 0;
     return (size_t)T * (size_t)Co * 2;

@@ -323,3 +323,57 @@ def test_power_of_two_row_scaling_and_permutation(reps):
     perm = rng.permutation(x.shape[0])
     permuted = dev_to_bits(sg.linear(bits_to_dev(np.ascontiguousarray(x[perm])), pw))
     assert np.array_equal(permuted, base[perm])
+
+
+# ---------------------------------------------------------------------------
+# split-K GEMM (ptpc_gemm_ws) for token counts with too few output tiles
+# ---------------------------------------------------------------------------
+def test_gemm_ws_split_k_ragged():
+    """K cut into ranges (here 4, the last one holding the K tail), rows and
+    columns ragged: whole output against the oracle, deterministic across
+    calls, and the workspace contents do not matter."""
+    T, Ci, Co = 100, 4112, 400
+    need = sg.gemm_workspace_bytes(T, Ci, Co)
+    assert need == 4 * 4 * T * Co
+    rng = np.random.default_rng(31)
+    x = workloads.random_bf16(rng, T, Ci, 1.0)
+    x[:, ::97] = workloads.f32_to_bf16_bits(workloads.bf16_bits_to_f32(x[:, ::97]) * np.float32(30))
+    w = workloads.random_bf16(rng, Ci, Co, 0.02)
+    qx, dx = sg.quant_act(bits_to_dev(x))
+    pw = sg.quant_weight(bits_to_dev(w))
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")     # NaN-pattern garbage
+    a = dev_to_bits(sg.gemm_ws(qx, dx, pw, workspace=ws))
+    b = dev_to_bits(sg.gemm_ws(qx, dx, pw))
+    qx_o, dx_o = oracle.quant_act(x)
+    qw_o, dw_o = oracle.quant_weight(w)
+    ref = oracle.apply_scales(oracle.gemm_exact(qx_o, qw_o), dx_o, dw_o)
+    check_close(a, ref, "split-K ragged")
+    assert np.array_equal(a, b), "split-K not deterministic"
+
+
+def test_gemm_ws_sweep_t128():
+    """The 70B layers at 128 tokens through ptpc_gemm_ws (QKV: 3 K ranges,
+    O and down: 4, gate_up: no split -> bit-identical to ptpc_gemm)."""
+    for layer in workloads.SWEEP_LAYERS:
+        shape, x, w = workloads.make("70b_sweep", T=128, layer=layer)
+        note(f"split-K 70b {layer} T=128")
+        qx, dx = sg.quant_act(bits_to_dev(x))
+        pw = sg.quant_weight(bits_to_dev(w))
+        out = dev_to_bits(sg.gemm_ws(qx, dx, pw))
+        plain = dev_to_bits(sg.gemm(qx, dx, pw))
+        if sg.gemm_workspace_bytes(128, shape.Ci, shape.Co) == 0:
+            assert np.array_equal(out, plain)
+            continue
+        qx_o, dx_o = oracle.quant_act(x)
+        qw_o, dw_o = oracle.quant_weight(w)
+        rows, cols = sample_indices(128, shape.Co, 3000, seed=3)
+        ref = oracle_sampled_ref(qx_o, dx_o, qw_o, dw_o, rows, cols)
+        check_close(out[rows, cols], ref, f"{shape.name} split-K (sampled)")
+        # another fp32 summation order than ptpc_gemm: equal up to a bf16 ulp
+        d = np.abs(bf16_f32(out) - bf16_f32(plain))
+        assert d.max() <= 2.0 ** -7 * np.abs(bf16_f32(plain)).max()
+        del qx, dx, pw
+
+
+def bf16_f32(b):
+    return workloads.bf16_bits_to_f32(b).astype(np.float64)
