@@ -161,6 +161,17 @@ def cpu_baseline(x_bits, w_bits, target_s):
                        f"(weight quantization {t_w:.1f} s); {nthr} OpenMP threads")}
 
 
+def no_nan(v):
+    """JSON has no NaN: stages that did not run (--only) report null."""
+    if isinstance(v, float) and v != v:
+        return None
+    if isinstance(v, dict):
+        return {k: no_nan(x) for k, x in v.items()}
+    if isinstance(v, list):
+        return [no_nan(x) for x in v]
+    return v
+
+
 def act_bytes_ref(T, Ci):
     """Bytes a bf16 -> 1-byte cast of a [T x Ci] matrix moves."""
     return 3.0 * T * Ci
@@ -440,13 +451,15 @@ def main():
         ev[1].record(stream)
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) * 1e-3 / n
-    cp_src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
-    cp_dst = torch.empty_like(cp_src)
-    copy_gbs = 2.0 * cp_src.numel() / timed(lambda: cp_dst.copy_(cp_src)) / 1e9
-    del cp_src, cp_dst
-    cast_dst = torch.empty((T, Ci), dtype=torch.float8_e4m3fn, device=dev)
-    cast_gbs = act_bytes_ref(T, Ci) / timed(lambda: cast_dst.copy_(x)) / 1e9
-    del cast_dst
+    copy_gbs = cast_gbs = float("nan")
+    if not args.only:
+        cp_src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        cp_dst = torch.empty_like(cp_src)
+        copy_gbs = 2.0 * cp_src.numel() / timed(lambda: cp_dst.copy_(cp_src)) / 1e9
+        del cp_src, cp_dst
+        cast_dst = torch.empty((T, Ci), dtype=torch.float8_e4m3fn, device=dev)
+        cast_gbs = act_bytes_ref(T, Ci) / timed(lambda: cast_dst.copy_(x)) / 1e9
+        del cast_dst
 
     per_stage = {s: [] for s in stages}
     for ev in events:
@@ -536,7 +549,7 @@ def main():
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    print(json.dumps(no_nan(result)), flush=True)
 
 
 if __name__ == "__main__":
