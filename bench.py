@@ -46,6 +46,10 @@ def parse():
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="run a plain device copy of this many MiB (3x) before timing, "
                         "as the reference kernel for HBM byte counters")
+    p.add_argument("--scaled-mm-context", action="store_true",
+                   help="context only: time torch._scaled_mm (hipBLASLt) in the pages' two forms "
+                        "(row-wise scales; unit scales + two multiplies) and per-tensor, on the "
+                        "same quantized data as ptpc_gemm (one JSON line)")
     p.add_argument("--model-load", action="store_true",
                    help="quantize + prepack every linear weight of the 80 Llama-3.1-70B "
                         "decoder layers and report the load-time cost (one JSON line)")
@@ -227,6 +231,70 @@ def model_load(args):
     }), flush=True)
 
 
+def scaled_mm_context(args):
+    """torch._scaled_mm (hipBLASLt) on the same quantized operands as
+    ptpc_gemm, in the two forms the pages show -- the fused call with
+    row-wise token / channel scales, and the naive one (unit scales, then a
+    multiply by each scale vector) -- and with per-tensor scales.  Context
+    only: nothing in the library calls it."""
+    import numpy as np
+    import torch
+
+    import scaled_gemm_amd as sg
+    import workloads
+
+    dev = torch.device("cuda:0")
+    sg.lib()
+    if args.workload == "70b_sweep":
+        shape, xb, wb = workloads.make("70b_sweep", T=args.T or 8192, layer=args.layer or "gate_up")
+    else:
+        shape, xb, wb = workloads.make(args.workload, T=args.T)
+    T, Ci, Co = shape.T, shape.Ci, shape.Co
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).to(dev)
+    del xb, wb
+    qx, dx = sg.quant_act(x)
+    pw = sg.quant_weight(w)
+    a8 = qx.view(torch.float8_e4m3fn)
+    b8 = sg.unpack_weight(pw).t().contiguous().view(torch.float8_e4m3fn).t()  # column-major
+    sa, sb = dx.view(T, 1).contiguous(), pw.dw.view(1, Co).contiguous()
+    one = torch.ones((), dtype=torch.float32, device=dev)
+    out = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((max(1, sg.gemm_workspace_bytes(T, Ci, Co)),), dtype=torch.uint8, device=dev)
+    calls = {
+        "ptpc_gemm": lambda: sg.gemm(qx, dx, pw, out=out),
+        "ptpc_gemm_ws": lambda: sg.gemm_ws(qx, dx, pw, out=out, workspace=ws),
+        "scaled_mm_rowwise": lambda: torch._scaled_mm(a8, b8, scale_a=sa, scale_b=sb,
+                                                      out_dtype=torch.bfloat16),
+        "scaled_mm_naive": lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one,
+                                                    out_dtype=torch.bfloat16) * sa * sb,
+        "scaled_mm_per_tensor": lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one,
+                                                         out_dtype=torch.bfloat16),
+    }
+    ms = {}
+    for k, fn in calls.items():
+        try:
+            for _ in range(max(3, args.warmup)):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            for _ in range(args.steps):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms[k] = ev[0].elapsed_time(ev[1]) / args.steps
+        except RuntimeError as e:                      # a form hipBLASLt does not support
+            ms[k] = None
+            print(f"# {k}: {e}", file=sys.stderr)
+    flops = 2.0 * T * Ci * Co
+    print(json.dumps({
+        "what": "context only: torch._scaled_mm (hipBLASLt) on the same quantized data",
+        "workload": shape.name, "T": T, "Ci": Ci, "Co": Co,
+        "ms": {k: (round(v, 4) if v else None) for k, v in ms.items()},
+        "tflops": {k: (round(flops / v / 1e9, 1) if v else None) for k, v in ms.items()},
+    }), flush=True)
+
+
 def sweep(args):
     """Per-shape kernel rates over every workload shape (HIP events around each
     launch on the launch stream, after a warm-up)."""
@@ -315,6 +383,9 @@ def main():
         return
     if args.model_load:
         model_load(args)
+        return
+    if args.scaled_mm_context:
+        scaled_mm_context(args)
         return
     if args.traffic_from:
         rec = traffic_record(args.traffic_from[0], args.traffic_from[1], args.workload,

@@ -128,13 +128,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     constexpr int A_BLK = BM / 8;                    // A pair: 8 rows x 128 B per load
     constexpr int B_BLK = BN / 16;                   // B step: 16 rows x 64 B per load
     constexpr int A_HALF_PER_W = A_BLK / 2 / NW;     // loads per wave per half pair
-    constexpr int B_PER_W = B_BLK / NW;
+    // When the B blocks do not split evenly over the waves, every wave still
+    // issues B_PER_W loads (the extra ones out of range, into padding at the
+    // end of the slot), so that all waves count the same loads.
+    constexpr int B_PER_W = (B_BLK + NW - 1) / NW;
     constexpr int DPW = A_HALF_PER_W + B_PER_W;      // loads per wave per step
-    static_assert(A_HALF_PER_W * 2 * NW == A_BLK && B_PER_W * NW == B_BLK, "tile/waves");
+    static_assert(A_HALF_PER_W * 2 * NW == A_BLK, "tile/waves");
     static_assert(NB == 3 || NB == 4, "B ring depth");
     static_assert((NB - 2) * DPW < 64, "vmcnt range");
     constexpr int A_SLOT = BM * 2 * BK;              // one pair slot
-    constexpr int B_SLOT = BN * BK;
+    constexpr int B_SLOT = B_PER_W * NW * 1024;      // BN * BK, padded to whole wave loads
     // Distinct LDS objects per slot (not one array indexed by slot) so that
     // the compiler can tell the slot being filled from the slot being read
     // and does not wait for fills before reads.
@@ -344,29 +347,32 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     // Each lane therefore owns runs of 4 consecutive columns of one row.
     if constexpr (FUSED) {
         // The bf16 results of one 32-row slab of the wave tile go to a
-        // wave-private LDS region (in the first A slot, idle now) and come
-        // back as 16-byte row chunks, so that every store instruction writes
-        // whole row segments of WTN*2 bytes.  Chunk c of slab row r sits at
-        // chunk c ^ ((r / RB) % NC) of its LDS row (RB rows span the 64
-        // banks), which spreads the 8-byte writes of one instruction (32
-        // rows, one column run) over all banks.
+        // wave-private LDS region (in the A slots, idle now) and come back as
+        // 16-byte row chunks, so that every store instruction writes whole
+        // row segments of WTN*2 bytes.  The 8-byte writes of one instruction
+        // (32 rows, one column run) are spread over all banks: with a
+        // power-of-two chunk count chunk c of slab row r sits at chunk
+        // c ^ ((r / RB) % NC) of its LDS row (RB rows span the 64 banks);
+        // otherwise rows are padded by 16 bytes.
         constexpr int P = WTN * 2;                   // bytes per slab row
         constexpr int NC = WTN / 8;                  // 16-byte chunks per row
-        constexpr int RB = 256 / P;
-        constexpr int RPI = 64 / NC;                 // rows per read instruction
-        // Wave regions of 32*P bytes, as many per A slot as fit, slots in
+        constexpr bool POW2 = (NC & (NC - 1)) == 0;
+        constexpr int PITCH = POW2 ? P : P + 16;
+        constexpr int RB = POW2 ? 256 / P : 1;
+        constexpr int NCHUNK = 32 * NC;              // chunks per slab
+        // Wave regions of 32*PITCH bytes, as many per A slot as fit, slots in
         // order (all three A slots are idle after the loop).
-        constexpr int RPS = A_SLOT / (32 * P);       // regions per A slot
-        static_assert(RPS >= 1 && NW <= 3 * RPS && RB >= 1 && RPI >= 1, "staging");
+        constexpr int RPS = A_SLOT / (32 * PITCH);   // regions per A slot
+        static_assert(RPS >= 1 && NW <= 3 * RPS && RB >= 1, "staging");
         const int sl = wave / RPS;
         uint8_t* const stage =
-            (sl == 0 ? a_s0 : sl == 1 ? a_s1 : a_s2) + (wave - sl * RPS) * (32 * P);
+            (sl == 0 ? a_s0 : sl == 1 ? a_s1 : a_s2) + (wave - sl * RPS) * (32 * PITCH);
+        auto slot_of = [](int r, int c) { return POW2 ? (c ^ ((r / RB) % NC)) : c; };
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             const int64_t row = m0 + wm * WTM + i * 32 + lr;
             const float sx =
                 (row < T) ? (scale_mode == kUnitScales ? 1.0f : dx[scale_mode ? 0 : row]) : 0.0f;
-            const int sw_r = (lr / RB) % NC;
 #pragma unroll
             for (int j = 0; j < NTL; ++j) {
 #pragma unroll
@@ -381,16 +387,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
                            ((uint32_t)f32_to_bf16_rne((a1 * sx) * sw.y) << 16);
                     pk.y = (uint32_t)f32_to_bf16_rne((a2 * sx) * sw.z) |
                            ((uint32_t)f32_to_bf16_rne((a3 * sx) * sw.w) << 16);
-                    const int c = 4 * j + g;
-                    *reinterpret_cast<uint2*>(stage + lr * P + ((c ^ sw_r) << 4) + lg * 8) = pk;
+                    *reinterpret_cast<uint2*>(stage + lr * PITCH + (slot_of(lr, 4 * j + g) << 4) +
+                                              lg * 8) = pk;
                 }
             }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-            for (int q = 0; q < 32 / RPI; ++q) {
-                const int rr = q * RPI + lane / NC, cc = lane % NC;
-                const uint4 v = *reinterpret_cast<const uint4*>(
-                    stage + rr * P + ((cc ^ ((rr / RB) % NC)) << 4));
+            for (int q = 0; q < (NCHUNK + 63) / 64; ++q) {
+                const int idx = q * 64 + lane;
+                const int rr = idx / NC, cc = idx % NC;
+                if (idx >= NCHUNK) continue;
+                const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * PITCH +
+                                                                (slot_of(rr, cc) << 4));
                 const int64_t grow = m0 + wm * WTM + i * 32 + rr;
                 const int64_t gcol = n0 + wn * WTN + cc * 8;
                 if (grow < T && gcol < Co)
@@ -688,6 +696,9 @@ static hipError_t launch_tiles(const uint8_t* qx, int64_t ldq, const float* dx, 
 #ifndef TILE_COST_256x128
 #define TILE_COST_256x128 0.69
 #endif
+#ifndef TILE_COST_256x224
+#define TILE_COST_256x224 0.92
+#endif
 #ifndef TILE_COST_192x256
 #define TILE_COST_192x256 0.88
 #endif
@@ -695,9 +706,10 @@ static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, c
                        const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                        int64_t ldo, float* fp32_out, hipStream_t s, int ts) {
     // Tile choice: 256x256 keeps the most MFMA work per loaded byte; when it
-    // leaves CUs idle or a badly filled last round, 192x256 or 256x128 (more
-    // tiles, each costing 0.88 or 0.69 of a 256x256 one, measured on the
-    // 1024-token 70B layers) is taken if its rounds cost less.
+    // leaves CUs idle or a badly filled last round, 256x224 (4 waves side by
+    // side along the tokens), 192x256 or 256x128 -- more tiles, each costing
+    // 0.92, 0.88 or 0.69 of a 256x256 one, measured on the 8B / 70B layers --
+    // is taken if its rounds cost less.
     auto rounds = [](int64_t tiles) { return (tiles + kCus - 1) / kCus; };
     auto tiles = [&](int64_t bm, int64_t bn) { return ((T + bm - 1) / bm) * ((Co + bn - 1) / bn); };
     // Cost in 256x256 tile-times of each tiled form: rounds of 256 CUs times
@@ -705,6 +717,7 @@ static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, c
     const double c256 = (double)rounds(tiles(256, 256));
     const double c128 = TILE_COST_256x128 * (double)rounds(tiles(256, 128));
     const double c192 = TILE_COST_192x256 * (double)rounds(tiles(192, 256));
+    const double c224 = TILE_COST_256x224 * (double)rounds(tiles(256, 224));
     // Up to 64 tokens the weight stream decides.  The tiled kernel reads
     // each weight byte once per row tile and keeps the activation in LDS, but
     // with few column tiles it leaves CUs idle; the few-token kernel splits K
@@ -714,7 +727,9 @@ static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, c
     // form (half the activation re-reads) pays off from 16 tokens on, once
     // the 32-column grid no longer fits the CUs in one round.
     hipError_t e;
-    if (T >= 256 && c128 < c256 && c128 <= c192)
+    if (T >= 256 && c224 < c256 && c224 < c192 && c224 < c128)
+        e = launch_tiles<256, 224, 4, 1, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+    else if (T >= 256 && c128 < c256 && c128 <= c192)
         e = launch_tiles<256, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T >= 256 && c192 < c256)
         e = launch_tiles<192, 256, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);

@@ -111,6 +111,7 @@ FULL_CASES = [
     ("ragged", 600, 256, 2048),
     ("ragged", 513, 512, 2064),
     ("ragged", 600, 144, 22000),
+    ("ragged", 500, 144, 28656),
 ]
 
 
