@@ -25,7 +25,7 @@
  *     Co % 16 == 0; base pointers 16-byte aligned; bf16 pitches multiples of
  *     8 elements and E4M3 pitches multiples of 16 (16-byte rows).  A zero
  *     extent is a no-op returning PTPC_OK (except as noted for Ci == 0).
- *     The GEMM calls also need Ci <= 2^22 and ldq <= 2^22.
+ *     The GEMM calls also need Ci, ldq and ldo <= 2^22.
  *     Anything else returns PTPC_ERR_UNSUPPORTED / PTPC_ERR_ALIGN.
  *
  * Quantization rule (readings taken where [PTPC] is silent):

@@ -155,54 +155,62 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
+    const int lr = lane & 31;
+    const int lg = lane >> 5;
     // Split K (splits > 1, two-step form only): workgroup b takes K range
     // b / ntiles of tile b % ntiles and writes its partial sums to slice
     // b / ntiles of the fp32 output.  Ranges are whole A pairs (even steps).
     const int gm = (int)((T + BM - 1) / BM), gn = (int)((Co + BN - 1) / BN);
     const int ntiles = gm * gn;
     const int split = (int)blockIdx.x / ntiles;
-    int tm, tn;
-    tile_of((int)blockIdx.x - split * ntiles, gm, gn, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
     const int nks = (int)(Kp / BK);                  // K steps of the packed weight (even)
     const int per = ((nks + splits - 1) / splits + 1) & ~1;
     const int ks0 = split * per < nks ? split * per : nks;
     const int nsteps = (ks0 + per < nks ? ks0 + per : nks) - ks0;
     const int64_t k_end = (int64_t)(ks0 + nsteps) * BK < Ci ? (int64_t)(ks0 + nsteps) * BK : Ci;
 
-    // Buffer descriptors based at this tile's first row and this split's
-    // first K step; rows past the end and K past the range land beyond
-    // num_records or are sent there, and read as zero.
-    const int64_t a_rows = (T - m0 < BM) ? (T - m0) : BM;
-    const int64_t b_rows = (Co - n0 < BN) ? (Co - n0) : BN;
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(qx + m0 * ldq + (int64_t)ks0 * BK, (uint32_t)(a_rows * ldq));
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(wp + n0 * Kp + (int64_t)ks0 * 1024, (uint32_t)(b_rows * Kp));
-
+    // Per-tile state.  Buffer descriptors are based at the tile's first row
+    // and the split's first K step; rows past the end and K past the range
+    // land beyond num_records or are sent there, and read as zero.
     // A pair load: lane L owns LDS row L/8 of its 8-row block, slot L%8, and
-    // fetches the logical chunk that belongs in that slot.
+    // fetches the logical chunk that belongs in that slot.  The packed
+    // weight is already in LDS order: 1 KB blocks of 16 columns x one 64-byte
+    // K step, lane L's 16 bytes at L*16 (see the packing kernel).
+    int64_t m0 = 0, n0 = 0, a_rows = 0;
+    __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t a_off[2][A_HALF_PER_W];
     int a_chunk[2][A_HALF_PER_W];
+    uint32_t b_off[B_PER_W];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int p = 0; p < A_HALF_PER_W; ++p) {
-            const int blk = h * (A_BLK / 2) + wave + p * NW;
-            const int r = blk * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ swz_a(r);
-            a_chunk[h][p] = c;
-            a_off[h][p] = (r < a_rows) ? (uint32_t)(r * ldq + c * 16) : kOutOfRange;
+            const int r = (h * (A_BLK / 2) + wave + p * NW) * 8 + (lane >> 3);
+            a_chunk[h][p] = (lane & 7) ^ swz_a(r);
         }
-    // The packed weight is already in LDS order: 1 KB blocks of 16 columns x
-    // one 64-byte K step, lane L's 16 bytes at L*16 (see the packing kernel).
-    uint32_t b_off[B_PER_W];
+    auto setup = [&](int tile) {
+        int tm, tn;
+        tile_of(tile, gm, gn, tm, tn);
+        m0 = (int64_t)tm * BM;
+        n0 = (int64_t)tn * BN;
+        a_rows = (T - m0 < BM) ? (T - m0) : BM;
+        const int64_t b_rows = (Co - n0 < BN) ? (Co - n0) : BN;
+        ra = make_rsrc(qx + m0 * ldq + (int64_t)ks0 * BK, (uint32_t)(a_rows * ldq));
+        rb = make_rsrc(wp + n0 * Kp + (int64_t)ks0 * 1024, (uint32_t)(b_rows * Kp));
 #pragma unroll
-    for (int p = 0; p < B_PER_W; ++p) {
-        const int blk = wave + p * NW;               // 16-column group in the tile
-        b_off[p] = (blk * 16 < b_rows) ? (uint32_t)(blk * nks * 1024 + lane * 16) : kOutOfRange;
-    }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int p = 0; p < A_HALF_PER_W; ++p) {
+                const int r = (h * (A_BLK / 2) + wave + p * NW) * 8 + (lane >> 3);
+                a_off[h][p] = (r < a_rows) ? (uint32_t)(r * ldq + a_chunk[h][p] * 16) : kOutOfRange;
+            }
+#pragma unroll
+        for (int p = 0; p < B_PER_W; ++p) {
+            const int blk = wave + p * NW;           // 16-column group in the tile
+            b_off[p] =
+                (blk * 16 < b_rows) ? (uint32_t)(blk * nks * 1024 + lane * 16) : kOutOfRange;
+        }
+    };
 
     // Loads of one half (h) of the A pair holding steps 2q, 2q+1.
     auto issue_a_half = [&](int q, int h, uint8_t* slot) {
@@ -228,17 +236,28 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
                 rb, (lds_ptr_t)(slot + (wave + p * NW) * 1024), 16, off, 0, 0, 0);
         }
     };
+    // The fills before step 0, as if issued at the tops of steps -NB .. -1:
+    // A pairs 0 and 1, the first NB B steps and the first half of A pair 2.
+    auto fill_part1 = [&]() {
+        issue_a_half(0, 0, a_slots[0]);
+        issue_a_half(0, 1, a_slots[0]);
+        issue_a_half(1, 0, a_slots[1]);
+        issue_a_half(1, 1, a_slots[1]);
+#pragma unroll
+        for (int u = 0; u < NB; ++u) issue_b(u, b_slots[u]);
+    };
+    auto fill_part2 = [&]() { issue_a_half(2, 0, a_slots[2]); };
 
     v16f acc[MT][NTL];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NTL; ++j)
+            for (int j = 0; j < NTL; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    };
 
-    const int lr = lane & 31;
-    const int lg = lane >> 5;
     // MFMA operands: lane l reads row l%32 of a 32-row slab and logical
     // chunks 2*(l/32), 2*(l/32)+1 of the 64-byte K step (for A, of the step's
     // half of the 128-byte pair row).
@@ -315,118 +334,143 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
         lds_barrier();
     };
 
-    // Steps past the data are zero fills (every offset out of range), so the
-    // loop needs no branch; it runs whole periods of P steps (fewer than P
-    // extra zero steps are multiplied).  Unrolled by the period so that every
-    // slot and fragment set is named statically.
+    // The K loop.  Steps past the data are zero fills (every offset out of
+    // range), so the loop needs no branch; it runs whole periods of P steps
+    // (fewer than P extra zero steps are multiplied).  Unrolled by the period
+    // so that every slot and fragment set is named statically.  On entry the
+    // operands of step 0 are in fr_a[0] / fr_b[0]; on exit no fill is in
+    // flight and every wave is past its last LDS read.
     constexpr int P = 6 * NB / gcd_c(6, NB);
-    if (nsteps > 0) {
-        // Fills as if issued at the tops of steps -NB .. -1.
-        issue_a_half(0, 0, a_slots[0]);
-        issue_a_half(0, 1, a_slots[0]);
-        issue_a_half(1, 0, a_slots[1]);
-        issue_a_half(1, 1, a_slots[1]);
-        issue_a_half(2, 0, a_slots[2]);
-#pragma unroll
-        for (int u = 0; u < NB; ++u) issue_b(u, b_slots[u]);
-        wait_counts<0, 0>();
-        lds_barrier();
-        read_frags(a_slots[0], 0, b_slots[0], fr_a[0], fr_b[0]);
+    auto k_loop = [&]() {
         for (int s0 = 0; s0 < nsteps; s0 += P) {
             [&]<int... Us>(std::integer_sequence<int, Us...>) {
                 ((top(), step(std::integral_constant<int, Us>{}, s0 + Us)), ...);
             }(std::make_integer_sequence<int, P>{});
         }
-        wait_counts<0, 0>();            // no fill may land after the loop
+        wait_counts<0, 0>();
         lds_barrier();
-    }
+    };
 
     // Epilogue.  The weight slab is the MFMA's first operand, so the 32x32
     // accumulator tile is out^T: in lane l, element e holds output row
     // (token) l%32 of the slab and output column 8*(e/4) + 4*(l/32) + e%4.
     // Each lane therefore owns runs of 4 consecutive columns of one row.
-    if constexpr (FUSED) {
-        // The bf16 results of one 32-row slab of the wave tile go to a
-        // wave-private LDS region (in the A slots, idle now) and come back as
-        // 16-byte row chunks, so that every store instruction writes whole
-        // row segments of WTN*2 bytes.  The 8-byte writes of one instruction
-        // (32 rows, one column run) are spread over all banks: with a
-        // power-of-two chunk count chunk c of slab row r sits at chunk
-        // c ^ ((r / RB) % NC) of its LDS row (RB rows span the 64 banks);
-        // otherwise rows are padded by 16 bytes.
-        constexpr int P = WTN * 2;                   // bytes per slab row
-        constexpr int NC = WTN / 8;                  // 16-byte chunks per row
-        constexpr bool POW2 = (NC & (NC - 1)) == 0;
-        constexpr int PITCH = POW2 ? P : P + 16;
-        constexpr int RB = POW2 ? 256 / P : 1;
-        constexpr int NCHUNK = 32 * NC;              // chunks per slab
-        // Wave regions of 32*PITCH bytes, as many per A slot as fit, slots in
-        // order (all three A slots are idle after the loop).
-        constexpr int RPS = A_SLOT / (32 * PITCH);   // regions per A slot
-        static_assert(RPS >= 1 && NW <= 3 * RPS && RB >= 1, "staging");
-        const int sl = wave / RPS;
-        uint8_t* const stage =
-            (sl == 0 ? a_s0 : sl == 1 ? a_s1 : a_s2) + (wave - sl * RPS) * (32 * PITCH);
-        auto slot_of = [](int r, int c) { return POW2 ? (c ^ ((r / RB) % NC)) : c; };
+    //
+    // Fused: the bf16 results of one 32-row slab of the wave tile go to a
+    // wave-private LDS region (in the A slots, idle now, from the last one
+    // down) and come back as 16-byte row chunks, so that every store
+    // instruction writes whole row segments of WTN*2 bytes.  The 8-byte
+    // writes of one instruction (32 rows, one column run) are spread over all
+    // banks: with a power-of-two chunk count chunk c of slab row r sits at
+    // chunk c ^ ((r / RB) % NC) of its LDS row (RB rows span the 64 banks);
+    // otherwise rows are padded by 16 bytes.  All scales are loaded up front
+    // (one latency instead of one per slab) and the stores go through a
+    // range-checked descriptor (rows past T land beyond it, columns past Co
+    // are sent there) instead of branches.
+    constexpr int P2 = WTN * 2;                      // bytes per slab row
+    constexpr int NC = WTN / 8;                      // 16-byte chunks per row
+    constexpr bool POW2 = (NC & (NC - 1)) == 0;
+    constexpr int PITCH = POW2 ? P2 : P2 + 16;
+    constexpr int RB = POW2 ? 256 / P2 : 1;
+    constexpr int NCHUNK = 32 * NC;                  // chunks per slab
+    constexpr int NSTORE = (NCHUNK + 63) / 64;       // store instructions per slab
+    constexpr int RPS = A_SLOT / (32 * PITCH);       // regions per A slot
+    static_assert(!FUSED || (RPS >= 1 && NW <= 3 * RPS && RB >= 1), "staging");
+    auto slot_of = [](int r, int c) { return POW2 ? (c ^ ((r / RB) % NC)) : c; };
+    float sxv[MT];
+    float4 swv[NTL][4];
+    auto load_scales = [&]() {
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             const int64_t row = m0 + wm * WTM + i * 32 + lr;
-            const float sx =
-                (row < T) ? (scale_mode == kUnitScales ? 1.0f : dx[scale_mode ? 0 : row]) : 0.0f;
+            sxv[i] = (scale_mode == kUnitScales || row >= T) ? 1.0f : dx[scale_mode ? 0 : row];
+        }
 #pragma unroll
-            for (int j = 0; j < NTL; ++j) {
+        for (int j = 0; j < NTL; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int64_t col = n0 + wn * WTN + j * 32 + 8 * g + 4 * lg;
-                    if (row >= T || col >= Co) continue;  // Co % 16 == 0: runs are whole
-                    const float a0 = acc[i][j][4 * g + 0], a1 = acc[i][j][4 * g + 1];
-                    const float a2 = acc[i][j][4 * g + 2], a3 = acc[i][j][4 * g + 3];
-                    const float4 sw = scale_of_cols(dw, col, scale_mode);
-                    uint2 pk;
-                    pk.x = (uint32_t)f32_to_bf16_rne((a0 * sx) * sw.x) |
-                           ((uint32_t)f32_to_bf16_rne((a1 * sx) * sw.y) << 16);
-                    pk.y = (uint32_t)f32_to_bf16_rne((a2 * sx) * sw.z) |
-                           ((uint32_t)f32_to_bf16_rne((a3 * sx) * sw.w) << 16);
-                    *reinterpret_cast<uint2*>(stage + lr * PITCH + (slot_of(lr, 4 * j + g) << 4) +
-                                              lg * 8) = pk;
+            for (int g = 0; g < 4; ++g) {
+                const int64_t col = n0 + wn * WTN + j * 32 + 8 * g + 4 * lg;
+                swv[j][g] = col < Co ? scale_of_cols(dw, col, scale_mode)
+                                     : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            }
+    };
+    auto epilogue = [&](int64_t em0, int64_t en0) {
+        if constexpr (FUSED) {
+            const int sl = wave / RPS;
+            uint8_t* const stage =
+                (sl == 0 ? a_s2 : sl == 1 ? a_s1 : a_s0) + (wave - sl * RPS) * (32 * PITCH);
+            const int64_t e_rows = (T - em0 < BM) ? (T - em0) : BM;
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(reinterpret_cast<uint16_t*>(out) + em0 * ldo, (uint32_t)(e_rows * ldo * 2));
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+#pragma unroll
+                for (int j = 0; j < NTL; ++j) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const float sx = sxv[i];
+                        const float4 sw = swv[j][g];
+                        uint2 pk;
+                        pk.x = (uint32_t)f32_to_bf16_rne((acc[i][j][4 * g + 0] * sx) * sw.x) |
+                               ((uint32_t)f32_to_bf16_rne((acc[i][j][4 * g + 1] * sx) * sw.y) << 16);
+                        pk.y = (uint32_t)f32_to_bf16_rne((acc[i][j][4 * g + 2] * sx) * sw.z) |
+                               ((uint32_t)f32_to_bf16_rne((acc[i][j][4 * g + 3] * sx) * sw.w) << 16);
+                        *reinterpret_cast<uint2*>(stage + lr * PITCH +
+                                                  (slot_of(lr, 4 * j + g) << 4) + lg * 8) = pk;
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+                for (int q = 0; q < NSTORE; ++q) {
+                    const int idx = q * 64 + lane;
+                    const int rr = idx / NC, cc = idx % NC;
+                    const bool in = idx < NCHUNK;
+                    const uint4 v = *reinterpret_cast<const uint4*>(
+                        stage + (in ? rr * PITCH + (slot_of(rr, cc) << 4) : 0));
+                    const int64_t lrow = wm * WTM + i * 32 + rr;      // row within the tile
+                    const int64_t gcol = en0 + wn * WTN + cc * 8;
+                    const uint32_t off = (in && gcol < Co)
+                                             ? (uint32_t)((lrow * ldo + gcol) * 2)
+                                             : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, ro, off, 0, 0);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            }
+        } else {
+            // Two-step form: unscaled fp32 runs of 4 columns, 16-byte stores.
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const int64_t row = em0 + wm * WTM + i * 32 + lr;
+                if (row >= T) continue;
+#pragma unroll
+                for (int j = 0; j < NTL; ++j) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int64_t col = en0 + wn * WTN + j * 32 + 8 * g + 4 * lg;
+                        if (col >= Co) continue;
+                        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) +
+                                                   (int64_t)split * T * Co + row * Co + col) =
+                            make_float4(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
+                                        acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+                    }
                 }
             }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-#pragma unroll
-            for (int q = 0; q < (NCHUNK + 63) / 64; ++q) {
-                const int idx = q * 64 + lane;
-                const int rr = idx / NC, cc = idx % NC;
-                if (idx >= NCHUNK) continue;
-                const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * PITCH +
-                                                                (slot_of(rr, cc) << 4));
-                const int64_t grow = m0 + wm * WTM + i * 32 + rr;
-                const int64_t gcol = n0 + wn * WTN + cc * 8;
-                if (grow < T && gcol < Co)
-                    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + grow * ldo +
-                                              gcol) = v;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
-    } else {
-        // Two-step form: unscaled fp32 runs of 4 columns, 16-byte stores.
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            const int64_t row = m0 + wm * WTM + i * 32 + lr;
-            if (row >= T) continue;
-#pragma unroll
-            for (int j = 0; j < NTL; ++j) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int64_t col = n0 + wn * WTN + j * 32 + 8 * g + 4 * lg;
-                    if (col >= Co) continue;
-                    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) +
-                                               (int64_t)split * T * Co + row * Co + col) =
-                        make_float4(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1],
-                                    acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-                }
-            }
-        }
+    };
+
+    setup((int)blockIdx.x - split * ntiles);
+    zero_acc();
+    if (nsteps > 0) {
+        fill_part1();
+        fill_part2();
+        wait_counts<0, 0>();
+        lds_barrier();
+        read_frags(a_slots[0], 0, b_slots[0], fr_a[0], fr_b[0]);
+        k_loop();
     }
+    if constexpr (FUSED) load_scales();
+    epilogue(m0, n0);
 }
 
 // Few tokens (T <= 64): the GEMM is a weight stream, bound by HBM.  A

@@ -96,10 +96,10 @@ static ptpc_status check_gemm(const uint8_t* qx, int64_t ldq, const float* dx,
                               int64_t Co, const void* out, int64_t ldo) {
     if (T < 0 || Ci < 0 || Co < 0 || ldq < Ci || ldo < Co) return PTPC_ERR_SHAPE;
     if (Ci % 16 != 0 || Co % 16 != 0) return PTPC_ERR_UNSUPPORTED;
-    // The kernels address an activation tile (<= 256 rows of ldq bytes) and a
-    // weight slab (<= 256 columns of roundup(Ci, 128) bytes) with 32-bit
-    // buffer offsets below 2^31.
-    if (ldq > kMaxGemmK || Ci > kMaxGemmK) return PTPC_ERR_UNSUPPORTED;
+    // The kernels address an activation tile (<= 256 rows of ldq bytes), a
+    // weight slab (<= 256 columns of roundup(Ci, 128) bytes) and an output
+    // tile (<= 256 rows of 2*ldo bytes) with 32-bit buffer offsets below 2^31.
+    if (ldq > kMaxGemmK || Ci > kMaxGemmK || ldo > kMaxGemmK) return PTPC_ERR_UNSUPPORTED;
     if (T == 0 || Co == 0) return PTPC_OK;
     if (dx == nullptr || dw == nullptr || out == nullptr ||
         (Ci > 0 && (qx == nullptr || w_packed == nullptr)))
