@@ -134,7 +134,6 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     constexpr int B_PER_W = (B_BLK + NW - 1) / NW;
     constexpr int DPW = A_HALF_PER_W + B_PER_W;      // loads per wave per step
     static_assert(A_HALF_PER_W * 2 * NW == A_BLK, "tile/waves");
-    static_assert(NB == 3 || NB == 4, "B ring depth");
     static_assert((NB - 2) * DPW < 64, "vmcnt range");
     constexpr int A_SLOT = BM * 2 * BK;              // one pair slot
     constexpr int B_SLOT = B_PER_W * NW * 1024;      // BN * BK, padded to whole wave loads
@@ -236,17 +235,33 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
                 rb, (lds_ptr_t)(slot + (wave + p * NW) * 1024), 16, off, 0, 0, 0);
         }
     };
-    // The fills before step 0, as if issued at the tops of steps -NB .. -1:
-    // A pairs 0 and 1, the first NB B steps and the first half of A pair 2.
-    auto fill_part1 = [&]() {
+    // The fills before step 0: A pairs 0 and 1, the first NB B steps and the
+    // first half of A pair 2, in the order they are needed, so that step 0
+    // can start once the first three have landed: with a and b loads per A
+    // half and per B step, the ones still allowed in flight then are the
+    // last 3a + 3b, and the K loop's own "all but the last 2 steps' loads"
+    // waits then see every later fill land before it is read (the loop's
+    // first three tops each retire a + b more of them in order).
+    static_assert(NB == 4, "fill order below is written for four B slots");
+    // (sched_barrier keeps the scheduler from reordering the groups.)
+    auto fill_prologue = [&]() {
         issue_a_half(0, 0, a_slots[0]);
         issue_a_half(0, 1, a_slots[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(0, b_slots[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(1, b_slots[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(2, b_slots[2]);
+        __builtin_amdgcn_sched_barrier(0);
         issue_a_half(1, 0, a_slots[1]);
         issue_a_half(1, 1, a_slots[1]);
-#pragma unroll
-        for (int u = 0; u < NB; ++u) issue_b(u, b_slots[u]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(3, b_slots[3]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a_half(2, 0, a_slots[2]);
+        __builtin_amdgcn_sched_barrier(0);
     };
-    auto fill_part2 = [&]() { issue_a_half(2, 0, a_slots[2]); };
 
     v16f acc[MT][NTL];
     auto zero_acc = [&]() {
@@ -462,9 +477,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     setup((int)blockIdx.x - split * ntiles);
     zero_acc();
     if (nsteps > 0) {
-        fill_part1();
-        fill_part2();
-        wait_counts<0, 0>();
+        fill_prologue();
+        wait_counts<3 * A_HALF_PER_W + 3 * B_PER_W, 0>();   // A pair 0 and B step 0
         lds_barrier();
         read_frags(a_slots[0], 0, b_slots[0], fr_a[0], fr_b[0]);
         k_loop();
@@ -552,6 +566,22 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
 
+    // The scales of the runs this wave stores at the end (see the epilogue),
+    // loaded before the K loop so that their latency hides behind it.
+    constexpr int NPW = (NT * MT * 4 + NWAVE - 1) / NWAVE;   // runs per wave
+    float sxp[NPW];
+    float4 swp[NPW];
+#pragma unroll
+    for (int k = 0; k < NPW; ++k) {
+        const int p = wave + k * NWAVE;
+        const int ji = p >> 2, g = p & 3;
+        const int j = ji / MT, i = ji - j * MT;
+        const int64_t row = i * 32 + lr;
+        const int64_t c = n0 + 32 * j + 8 * g + 4 * lg;
+        const bool ok = FUSED && p < NT * MT * 4 && row < T && c < Co;
+        sxp[k] = (!ok || scale_mode == kUnitScales) ? 1.0f : dx[scale_mode ? 0 : row];
+        swp[k] = ok ? scale_of_cols(dw, c, scale_mode) : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+    }
     const int count = (nks - wave + NWAVE - 1) / NWAVE;  // steps of this wave
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) load(u, wave + NWAVE * u);
@@ -586,7 +616,10 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
 #pragma unroll
             for (int e = 0; e < 16; ++e) red[wave][j * MT + i][e][lane] = acc[j][i][e];
     __syncthreads();
-    for (int p = wave; p < NT * MT * 4; p += NWAVE) {
+#pragma unroll
+    for (int k = 0; k < NPW; ++k) {
+        const int p = wave + k * NWAVE;
+        if (p >= NT * MT * 4) break;
         const int ji = p >> 2, g = p & 3;
         const int j = ji / MT, i = ji - j * MT;
         const int64_t row = i * 32 + lr;
@@ -602,8 +635,8 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
         const int64_t c = n0 + 32 * j + 8 * g + 4 * lg;
         if (row >= T || c >= Co) continue;
         if constexpr (FUSED) {
-            const float sx = scale_mode == kUnitScales ? 1.0f : dx[scale_mode ? 0 : row];
-            const float4 sw = scale_of_cols(dw, c, scale_mode);
+            const float sx = sxp[k];
+            const float4 sw = swp[k];
             uint2 pk;
             pk.x = (uint32_t)f32_to_bf16_rne((v[0] * sx) * sw.x) |
                    ((uint32_t)f32_to_bf16_rne((v[1] * sx) * sw.y) << 16);
