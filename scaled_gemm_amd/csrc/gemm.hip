@@ -19,15 +19,19 @@
 // both MFMA operands are read the same way: lane l takes row l % 32 of a
 // 32-row slab and 32 consecutive K bytes starting at 32 * (l / 32).
 //
-// Pipeline: tiles move HBM/L2 -> LDS with buffer_load_dwordx4 ... lds (no
-// staging registers, no ds_write); the buffer descriptor's range check
-// turns rows past T / Co and K past Ci into zeros.  LDS holds two stages;
-// while the MFMAs consume stage k, the loads for stage k+1 are in flight.
-// One LDS row is 128 bytes = 8 chunks of 16 bytes; chunk c of row r is
-// stored at slot c ^ swz(r), so the 32 rows an operand read touches spread
-// over the banks.  A load instruction fills 1 KB of LDS (64 lanes x 16 B,
-// i.e. 8 rows), so each lane fetches the global chunk that belongs in its
-// fixed LDS slot.
+// Pipeline (details above gemm_kernel): operand tiles move HBM/L2 -> LDS
+// with buffer_load_dwordx4 ... lds (no staging registers, no ds_write); the
+// buffer descriptor's range check turns rows past T / Co and K past Ci into
+// zeros.  LDS holds a ring of A and B slots several K steps deep.  Within an
+// LDS row, 16-byte chunk c of row r is stored at slot c ^ swz(r), so the 32
+// rows an operand read touches spread over the banks; a load instruction
+// fills 1 KB of LDS (64 lanes x 16 B), each lane fetching the global chunk
+// that belongs in its fixed LDS slot.
+//
+// Kernels: gemm_kernel (tiled, 32..256 x 64..256 output tiles, also the
+// split-K form), gemm_decode_kernel (up to 64 tokens: K split across the
+// waves of a workgroup), and the second passes of the two-step forms and of
+// split-K.
 #include <utility>
 
 #include "device_common.h"
