@@ -64,9 +64,18 @@ def parse():
 
 
 def gemm_source_hash():
-    src = os.path.join(ROOT, "scaled_gemm_amd", "csrc", "gemm.hip")
-    with open(src, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the GEMM's code: gemm.hip and the device header it includes,
+    with comments and blank space removed, so that the traffic record stays
+    valid across comment edits and is dropped on any code change."""
+    import re
+    text = ""
+    for name in ("gemm.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "scaled_gemm_amd", "csrc", name)) as f:
+            text += f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload):
