@@ -209,12 +209,24 @@ __global__ __launch_bounds__(256) void weight_colamax_kernel(
     if (r1 > Ci) r1 = Ci;
     us2 m0 = {0, 0}, m1 = {0, 0}, m2 = {0, 0}, m3 = {0, 0};
     if (col0 < Co) {
-        for (int64_t r = r0 + wave; r < r1; r += 4) {
-            uint4 v = *reinterpret_cast<const uint4*>(w + r * ldw + col0);
-            m0 = max2(m0, abs_bits2(v.x));
-            m1 = max2(m1, abs_bits2(v.y));
-            m2 = max2(m2, abs_bits2(v.z));
-            m3 = max2(m3, abs_bits2(v.w));
+        // Eight rows' loads in flight per wave before their maxes; rows past
+        // the split re-read its last row (the max is unchanged), so the loads
+        // need no branch.
+        constexpr int U = 8;
+        for (int64_t r = r0 + wave; r < r1; r += 4 * U) {
+            uint4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t rr = r + 4 * u < r1 ? r + 4 * u : r1 - 1;
+                v[u] = *reinterpret_cast<const uint4*>(w + rr * ldw + col0);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                m0 = max2(m0, abs_bits2(v[u].x));
+                m1 = max2(m1, abs_bits2(v[u].y));
+                m2 = max2(m2, abs_bits2(v[u].z));
+                m3 = max2(m3, abs_bits2(v[u].w));
+            }
         }
     }
     red[wave][lane][0] = m0;
@@ -267,14 +279,26 @@ __global__ __launch_bounds__(256) void weight_pack_kernel(
 
     Divisor dv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dv[j] = make_divisor(col_ok ? dw[(col + j) * dw_step] : 1.0f);
+    for (int j = 0; j < 8; ++j) {
+        const float d = dw[(col_ok ? col + j : 0) * dw_step];   // in bounds, no branch
+        dv[j] = make_divisor(col_ok ? d : 1.0f);
+    }
 
+    // All four rows' loads are issued before any is used: rows past Ci and
+    // columns past Co read a valid element (clamped address) and are then
+    // replaced by zero, so the loads need no branch.
+    uint4 vin[kPackK / 32];
+#pragma unroll
+    for (int p = 0; p < kPackK / 32; ++p) {
+        const int64_t k = k0 + p * 32 + rr;
+        const int64_t kc = k < Ci ? k : Ci - 1;
+        vin[p] = *reinterpret_cast<const uint4*>(w + kc * ldw + (col_ok ? col : 0));
+    }
 #pragma unroll
     for (int p = 0; p < kPackK / 32; ++p) {
         const int kl = p * 32 + rr;
         const int64_t k = k0 + kl;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (col_ok && k < Ci) v = *reinterpret_cast<const uint4*>(w + k * ldw + col);
+        const uint4 v = (col_ok && k < Ci) ? vin[p] : make_uint4(0, 0, 0, 0);
         const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {

@@ -115,6 +115,18 @@ FULL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("name,seed", [("tiny", 1), ("tiny", 2), ("8b_qkv_decode", 1),
+                                       ("8b_qkv_decode", 2)])
+def test_full_parity_other_seeds(name, seed):
+    note(f"full parity {name} seed={seed}")
+    _, x, w = workloads.make(name, seed=seed)
+    g = run_path(x, w)
+    qx, dx, qw, dw = check_quant(g, x, w, f"{name} seed {seed}")
+    ref = oracle.apply_scales(oracle.gemm_exact(qx, qw), dx, dw)
+    check_close(g["out"], ref, f"{name} seed {seed} fused")
+    assert np.array_equal(g["out"], g["out2"]), "fused and two-step differ"
+
+
 @pytest.mark.parametrize("name,T,Ci,Co", FULL_CASES)
 def test_full_parity(name, T, Ci, Co):
     note(f"full parity {name} T={T} Ci={Ci} Co={Co}")
@@ -324,6 +336,17 @@ def test_power_of_two_row_scaling_and_permutation(reps):
     perm = rng.permutation(x.shape[0])
     permuted = dev_to_bits(sg.linear(bits_to_dev(np.ascontiguousarray(x[perm])), pw))
     assert np.array_equal(permuted, base[perm])
+    # a weight column times 2^k: same codes, its scale and output column times 2^k
+    ws = workloads.bf16_bits_to_f32(w).copy()
+    ws[:, 5] *= np.float32(4)
+    ws[:, 17] *= np.float32(0.25)
+    pw2 = sg.quant_weight(bits_to_dev(workloads.f32_to_bf16_bits(ws)))
+    col = dev_to_bits(sg.linear(bits_to_dev(x), pw2))
+    c = (col.astype(np.uint32) << 16).view(np.float32)
+    want = b.copy()
+    want[:, 5] *= np.float32(4)
+    want[:, 17] *= np.float32(0.25)
+    assert np.array_equal(c, want)
 
 
 # ---------------------------------------------------------------------------
