@@ -8,7 +8,8 @@
 //
 // out[t,o] = bf16((acc[t,o] * dx[t]) * dw[o]),
 // acc[t,o] = sum_k qx[t,k] * qw[k,o] on OCP E4M3 values, fp32 accumulation
-// in v_mfma_f32_32x32x64_f8f6f4.
+// in v_mfma_f32_16x16x128_f8f6f4 (256-token tiles) or
+// v_mfma_f32_32x32x64_f8f6f4 (the other kernels).
 //
 // Data layout: qx is [T x Ci] row-major (K contiguous).  The packed weight
 // is a sequence of 1 KB blocks, [Co/16][Kp/64] of them (Kp = roundup(Ci,
@@ -17,7 +18,9 @@
 // LDS (16 rows of 64 bytes, chunks in swizzled slots), so B tiles stream as
 // contiguous 1 KB reads.  In LDS both operands are "rows of 64 K bytes" and
 // both MFMA operands are read the same way: lane l takes row l % 32 of a
-// 32-row slab and 32 consecutive K bytes starting at 32 * (l / 32).
+// 32-row slab and 32 consecutive K bytes starting at 32 * (l / 32) of a
+// 64-byte step (32x32x64), or row l % 16 of a 16-row slab and K bytes
+// 32 * (l / 16) .. +31 of a 128-byte step (16x16x128).
 //
 // Pipeline (details above gemm_kernel): operand tiles move HBM/L2 -> LDS
 // with buffer_load_dwordx4 ... lds (no staging registers, no ds_write); the
@@ -28,10 +31,11 @@
 // fills 1 KB of LDS (64 lanes x 16 B), each lane fetching the global chunk
 // that belongs in its fixed LDS slot.
 //
-// Kernels: gemm_kernel (tiled, 32..256 x 64..256 output tiles, also the
-// split-K form), gemm_decode_kernel (up to 64 tokens: K split across the
-// waves of a workgroup), and the second passes of the two-step forms and of
-// split-K.
+// Kernels: gemm16_kernel (tiled, 192..256-token x 128..256-column tiles,
+// 16x16x128 MFMAs), gemm_kernel (tiled, 32x64 and 128x128 tiles and the
+// split-K form, 32x32x64 MFMAs), gemm_decode_kernel (up to 64 tokens: K split
+// across the waves of a workgroup), and the second passes of the two-step
+// forms and of split-K.
 #include <utility>
 
 #include "device_common.h"
@@ -491,6 +495,345 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
     epilogue(m0, n0);
 }
 
+// The 16x16x128 form of the tiled kernel, used for the 256-token tiles.
+// Same operands, layouts and epilogue arithmetic as gemm_kernel, but every
+// MFMA is v_mfma_f32_16x16x128_f8f6f4: for the same work that form holds a
+// higher clock under the chip's power limit than the 32x32x64 one.  One MFMA
+// spans 128 K bytes, so a step is 128 K bytes: one A pair row (both halves)
+// and two 64-byte B blocks per 16 columns.
+//   LDS: 2 A slots (BM x 128 B) and 3 B slots (two 64-byte half steps of BN
+//   columns each); the weight, streamed from HBM, gets the deeper ring.
+//   Operand lanes: lane l takes row l % 16 of a 16-row slab and K bytes
+//   32 * (l / 16) .. +31 of the step (for B: from half step l / 32).
+//   A step runs over the wave's 16-column slabs j, each against all its
+//   16-row slabs (MT MFMAs).  The A fragments of step s+1 are read during
+//   step s (two register sets); the B fragment of slab j is read two slabs
+//   ahead of its use into a ring of three (the last two slabs of step s read
+//   step s+1's first two).  One piece of this side work (an operand read or
+//   a fill) follows each MFMA, so that its issue hides under the running
+//   MFMA.
+//   Two barriers per step.  At the top of step s, A of step s+1 has landed
+//   (it is read during step s) and A slot s%2 is free: A of step s+2 is
+//   filled into it during the first two slabs.  Before slab NT-2 ("mid"), B
+//   of step s+1 has landed (its first fragments are read next) and every read
+//   of B slot s%3 is done: B of step s+3 is filled into it during the last
+//   two slabs.  With loads issued in that order the waits are "all but the
+//   last step's B fills" at the top and "all but two A and one B fill
+//   groups" at mid.
+//   The MFMAs are issued from inline asm with the accumulators tied to AGPRs:
+//   with the builtin, the register allocator moved 64 four-register
+//   accumulators between AGPRs, VGPRs and scratch inside the K loop.  Inline
+//   asm hides the MFMAs from the compiler's hazard tracking, so the kernel
+//   keeps every dependence on an accumulator far apart by construction: in
+//   the K loop an accumulator is next used a full step later, the zeroing
+//   before the loop is pinned ahead of an explicit wait, and the epilogue
+//   reads the accumulators only after the loop's final wait and barrier.
+//   Operand registers are only read by the MFMAs (LDS loads may overwrite
+//   them right after issue, as in compiler-scheduled code).
+// The K loop runs whole periods of 6 steps; steps past the data are zero
+// fills.
+template <int BM, int BN, int WM, int WN, bool FUSED>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
+    const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
+    const uint8_t* __restrict__ wp, int64_t Kp, const float* __restrict__ dw,
+    int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo, int scale_mode,
+    int splits) {
+    constexpr int KS = 128;                          // K bytes per step
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int MT = WTM / 16, NT = WTN / 16;
+    constexpr int A_BLK = BM / 8;                    // A: 8 rows x 128 B per load
+    constexpr int BH = BN / 16;                      // B: 1 KB blocks per half step
+    constexpr int B_BLK = 2 * BH;
+    constexpr int A_PER_W = A_BLK / NW;
+    constexpr int B_PER_W = (B_BLK + NW - 1) / NW;   // padded: extra loads out of range
+    constexpr int RING = 3;                          // B fragment ring, read 2 slabs ahead
+    static_assert(A_PER_W * NW == A_BLK && NT >= 4, "tile/waves");
+    static_assert(2 * A_PER_W + 2 * B_PER_W < 64, "vmcnt range");
+    constexpr int A_SLOT = BM * KS;
+    constexpr int B_SLOT = B_PER_W * NW * 1024;
+    __shared__ __attribute__((aligned(1024))) uint8_t a_s0[A_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t a_s1[A_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t b_s0[B_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t b_s1[B_SLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t b_s2[B_SLOT];
+    auto a_slot = [&](int k) __attribute__((always_inline)) -> uint8_t* {
+        return k == 0 ? a_s0 : a_s1;
+    };
+    auto b_slot = [&](int k) __attribute__((always_inline)) -> uint8_t* {
+        return k == 0 ? b_s0 : k == 1 ? b_s1 : b_s2;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int l16 = lane & 15;
+    const int lg = lane >> 4;
+    const int gm = (int)((T + BM - 1) / BM), gn = (int)((Co + BN - 1) / BN);
+    const int ntiles = gm * gn;
+    const int split = (int)blockIdx.x / ntiles;
+    const int nks = (int)(Kp / KS);
+    const int per = (nks + splits - 1) / splits;
+    const int ks0 = split * per < nks ? split * per : nks;
+    const int nsteps = (ks0 + per < nks ? ks0 + per : nks) - ks0;
+    const int64_t k_end = (int64_t)(ks0 + nsteps) * KS < Ci ? (int64_t)(ks0 + nsteps) * KS : Ci;
+
+    // Loads.  A: load p of a wave covers the 8-row block wave + p * NW; lane
+    // L owns LDS row L/8 of it, slot L%8, and fetches the logical chunk that
+    // belongs there.  B: load p copies 1 KB packed block bl = wave + p * NW
+    // of the step (16-column group bl % BH, half step bl / BH) to LDS offset
+    // bl * 1024.  Offsets are 32-bit (the descriptors span less than 4 GB)
+    // and branch-free.
+    int tm, tn;
+    tile_of((int)blockIdx.x - split * ntiles, gm, gn, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+    const int64_t a_rows = (T - m0 < BM) ? (T - m0) : BM;
+    const int64_t b_rows = (Co - n0 < BN) ? (Co - n0) : BN;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(qx + m0 * ldq + (int64_t)ks0 * KS, (uint32_t)(a_rows * ldq));
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(wp + n0 * Kp + (int64_t)ks0 * 2048, (uint32_t)(b_rows * Kp));
+    const int k_lim = (int)(k_end - (int64_t)ks0 * KS);  // K bytes of this range
+    // With an even number of waves, the A rows of load p are those of load 0
+    // plus p * NW * 8 and their chunk swizzle is the same, so the per-lane
+    // part of every A offset is one register; the rest is wave-uniform.
+    static_assert(NW % 2 == 0, "A chunk swizzle shared by all loads of a wave");
+    const int a_r0 = wave * 8 + (lane >> 3);
+    const int a_c16 = ((lane & 7) ^ swz_a(a_r0)) * 16;
+    const uint32_t a_lane = (uint32_t)a_r0 * (uint32_t)ldq + (uint32_t)a_c16;
+    const uint32_t b_lane = (uint32_t)lane * 16u;
+    auto issue_a = [&](int ks, int p, uint8_t* slot) __attribute__((always_inline)) {
+        const int k0 = ks * KS;
+        const bool in = (a_r0 + p * NW * 8 < (int)a_rows) & (k0 + a_c16 < k_lim);
+        const uint32_t off =
+            in ? a_lane + (uint32_t)(p * NW * 8) * (uint32_t)ldq + (uint32_t)k0 : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + (wave + p * NW) * 1024),
+                                                 16, off, 0, 0, 0);
+    };
+    auto issue_b = [&](int ks, int p, uint8_t* slot) __attribute__((always_inline)) {
+        const int bl = wave + p * NW;
+        const int blk = bl % BH, h = bl / BH;
+        const bool in = (bl < B_BLK) & (blk * 16 < (int)b_rows) & (ks < nsteps);
+        const uint32_t off =
+            in ? b_lane + ((uint32_t)(blk * 16) * (uint32_t)Kp + (uint32_t)(h * 1024 + ks * 2048))
+               : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + bl * 1024), 16, off, 0,
+                                                 0, 0);
+    };
+
+    // Operand reads (see the layout above); the swizzle of a 16-row slab
+    // depends only on the lane, slabs are fixed offsets apart.
+    const int a_lo = (wm * WTM + l16) * KS + (((2 * lg) ^ swz_a(l16)) << 4);
+    const int a_hi = (wm * WTM + l16) * KS + (((2 * lg + 1) ^ swz_a(l16)) << 4);
+    const int b_base = (lg >> 1) * BH * 1024 + (wn * WTN + l16) * 64;
+    const int b_lo = b_base + (((2 * (lg & 1)) ^ swz_b(l16)) << 4);
+    const int b_hi = b_base + (((2 * (lg & 1) + 1) ^ swz_b(l16)) << 4);
+    auto read_a = [&](const uint8_t* as, int i) __attribute__((always_inline)) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(as + a_lo + i * 16 * KS);
+        const uint4 hi = *reinterpret_cast<const uint4*>(as + a_hi + i * 16 * KS);
+        return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    auto read_b = [&](const uint8_t* bs, int j) __attribute__((always_inline)) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(bs + b_lo + j * 1024);
+        const uint4 hi = *reinterpret_cast<const uint4*>(bs + b_hi + j * 1024);
+        return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+
+    // Accumulators: zeroed, pinned (the empty asm makes every zero write
+    // happen before it) and followed by a wait before any MFMA reads them.
+    v4f acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            asm volatile("" : "+a"(acc[i][j]));
+        }
+    asm volatile("s_nop 4");
+    v8i fr_a[2][MT], fr_b[RING];
+
+    auto sync = [&](auto VM) __attribute__((always_inline)) {
+        wait_counts<decltype(VM)::value, 0>();
+        lds_barrier();
+    };
+    // Step s = s0 + u (u = s % 6 static): slab by slab, each slab's MFMAs with
+    // its side work threaded between them (see above).
+    auto step = [&](auto U, int s) __attribute__((always_inline)) {
+        constexpr int u = decltype(U)::value;
+        constexpr int cur = u & 1;
+        const uint8_t* const na = a_slot((u + 1) % 2);
+        const uint8_t* const cb = b_slot(u % 3);
+        const uint8_t* const nb = b_slot((u + 1) % 3);
+        uint8_t* const fa = a_slot(u % 2);
+        uint8_t* const fb = b_slot(u % 3);
+        [&]<int... Js>(std::integer_sequence<int, Js...>) __attribute__((always_inline)) {
+            ([&]() __attribute__((always_inline)) {
+                constexpr int j = Js;
+                constexpr int g = u * NT + j;                 // global slab index
+                constexpr int ia0 = j * MT / NT, ia1 = (j + 1) * MT / NT;  // A frags read
+                constexpr int NE = NT - 2;                    // slabs before mid
+                constexpr int pa0 = j < 2 ? j * A_PER_W / 2 : 0;               // A fills
+                constexpr int pa1 = j < 2 ? (j + 1) * A_PER_W / 2 : 0;
+                constexpr int pb0 = j < NE ? 0 : (j - NE) * B_PER_W / 2;       // B fills
+                constexpr int pb1 = j < NE ? 0 : (j - NE + 1) * B_PER_W / 2;
+                if constexpr (j == NE) sync(std::integral_constant<int, 2 * A_PER_W + B_PER_W>{});
+                // Side work of the slab in issue order: the A fragments and
+                // the B fragment first, then the fills.
+                constexpr int NIA = ia1 - ia0, NPA = pa1 - pa0, NPB = pb1 - pb0;
+                constexpr int NITEM = NIA + 1 + NPA + NPB;
+                auto side = [&](auto Q) __attribute__((always_inline)) {
+                    constexpr int q = decltype(Q)::value;
+                    if constexpr (q < NIA) {
+                        fr_a[cur ^ 1][ia0 + q] = read_a(na, ia0 + q);
+                    } else if constexpr (q == NIA) {
+                        if constexpr (j + 2 < NT)
+                            fr_b[(g + 2) % RING] = read_b(cb, j + 2);
+                        else
+                            fr_b[(g + 2) % RING] = read_b(nb, j + 2 - NT);
+                    } else if constexpr (q < NIA + 1 + NPA) {
+                        issue_a(s + 2, pa0 + q - NIA - 1, fa);
+                    } else if constexpr (q < NITEM) {
+                        issue_b(s + 3, pb0 + q - NIA - 1 - NPA, fb);
+                    }
+                };
+                __builtin_amdgcn_sched_barrier(0);
+                [&]<int... Qs>(std::integer_sequence<int, Qs...>) __attribute__((always_inline)) {
+                    ([&]() __attribute__((always_inline)) {
+                        constexpr int q = Qs;
+                        if constexpr (q < MT)
+                            asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0"
+                                         : "+a"(acc[q][j])
+                                         : "v"(fr_b[g % RING]), "v"(fr_a[cur][q]));
+                        __builtin_amdgcn_sched_barrier(0);
+                        side(std::integral_constant<int, q>{});
+                        __builtin_amdgcn_sched_barrier(0);
+                    }(), ...);
+                }(std::make_integer_sequence<int, (MT > NITEM ? MT : NITEM)>{});
+                __builtin_amdgcn_sched_barrier(0);
+            }(), ...);
+        }(std::make_integer_sequence<int, NT>{});
+    };
+
+    if (nsteps > 0) {
+        // Fills in steady-state order: B0, A0, B1, A1, B2.
+#pragma unroll
+        for (int p = 0; p < B_PER_W; ++p) issue_b(0, p, b_s0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < A_PER_W; ++p) issue_a(0, p, a_s0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < B_PER_W; ++p) issue_b(1, p, b_s1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < A_PER_W; ++p) issue_a(1, p, a_s1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < B_PER_W; ++p) issue_b(2, p, b_s2);
+        __builtin_amdgcn_sched_barrier(0);
+        sync(std::integral_constant<int, A_PER_W + 2 * B_PER_W>{});   // A0, B0
+#pragma unroll
+        for (int i = 0; i < MT; ++i) fr_a[0][i] = read_a(a_s0, i);
+        fr_b[0] = read_b(b_s0, 0);
+        fr_b[1] = read_b(b_s0, 1);
+        constexpr int P = 6;
+        for (int s0 = 0; s0 < nsteps; s0 += P) {
+            [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
+                ((sync(std::integral_constant<int, B_PER_W>{}),
+                  step(std::integral_constant<int, Us>{}, s0 + Us)),
+                 ...);
+            }(std::make_integer_sequence<int, P>{});
+        }
+        wait_counts<0, 0>();
+        lds_barrier();
+    }
+
+    // Epilogue.  The weight slab is the MFMA's first operand, so the 16x16
+    // accumulator tile is out^T: in lane l, element e holds token row l % 16
+    // of the slab and column 4 * (l / 16) + e.  As in gemm_kernel, the bf16
+    // results of one 16-row slab go through a wave-private LDS region (in
+    // A slot 0) and leave as 16-byte row chunks through a range-checked
+    // descriptor.
+    constexpr int P2 = WTN * 2;
+    constexpr int NC = WTN / 8;
+    constexpr bool POW2 = (NC & (NC - 1)) == 0;
+    constexpr int PITCH = POW2 ? P2 : P2 + 16;
+    constexpr int RB = POW2 ? (256 / P2 > 0 ? 256 / P2 : 1) : 1;
+    constexpr int NCHUNK = 16 * NC;
+    constexpr int NSTORE = (NCHUNK + 63) / 64;
+    static_assert(!FUSED || NW * 16 * PITCH <= A_SLOT, "staging");
+    auto slot_of = [](int r, int c) { return POW2 ? (c ^ ((r / RB) % NC)) : c; };
+    if constexpr (FUSED) {
+        float sxv[MT];
+        float4 swv[NT];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const int64_t row = m0 + wm * WTM + i * 16 + l16;
+            sxv[i] = (scale_mode == kUnitScales || row >= T) ? 1.0f : dx[scale_mode ? 0 : row];
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int64_t col = n0 + wn * WTN + j * 16 + 4 * lg;
+            swv[j] = col < Co ? scale_of_cols(dw, col, scale_mode)
+                              : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        }
+        uint8_t* const stage = a_s0 + wave * (16 * PITCH);
+        const int64_t e_rows = (T - m0 < BM) ? (T - m0) : BM;
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(reinterpret_cast<uint16_t*>(out) + m0 * ldo, (uint32_t)(e_rows * ldo * 2));
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const float sx = sxv[i];
+                const float4 sw = swv[j];
+                uint2 pk;
+                pk.x = (uint32_t)f32_to_bf16_rne((acc[i][j][0] * sx) * sw.x) |
+                       ((uint32_t)f32_to_bf16_rne((acc[i][j][1] * sx) * sw.y) << 16);
+                pk.y = (uint32_t)f32_to_bf16_rne((acc[i][j][2] * sx) * sw.z) |
+                       ((uint32_t)f32_to_bf16_rne((acc[i][j][3] * sx) * sw.w) << 16);
+                *reinterpret_cast<uint2*>(stage + l16 * PITCH +
+                                          (slot_of(l16, 2 * j + (lg >> 1)) << 4) +
+                                          (lg & 1) * 8) = pk;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+            for (int q = 0; q < NSTORE; ++q) {
+                const int idx = q * 64 + lane;
+                const int rr = idx / NC, cc = idx % NC;
+                const bool in = idx < NCHUNK;
+                const uint4 v = *reinterpret_cast<const uint4*>(
+                    stage + (in ? rr * PITCH + (slot_of(rr, cc) << 4) : 0));
+                const int64_t lrow = wm * WTM + i * 16 + rr;
+                const int64_t gcol = n0 + wn * WTN + cc * 8;
+                const uint32_t off =
+                    (in && gcol < Co) ? (uint32_t)((lrow * ldo + gcol) * 2) : kOutOfRange;
+                __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w},
+                                                       ro, off, 0, 0);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const int64_t row = m0 + wm * WTM + i * 16 + l16;
+            if (row >= T) continue;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int64_t col = n0 + wn * WTN + j * 16 + 4 * lg;
+                if (col >= Co) continue;
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) +
+                                           (int64_t)split * T * Co + row * Co + col) =
+                    make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            }
+        }
+    }
+}
+
 // Few tokens (T <= 64): the GEMM is a weight stream, bound by HBM.  A
 // workgroup owns NT*32 output columns and all T rows (MT = ceil(T/32) row
 // tiles of 32); its NWAVE waves split the K steps (wave w takes steps w,
@@ -774,6 +1117,23 @@ static hipError_t launch_tiles(const uint8_t* qx, int64_t ldq, const float* dx, 
     return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN>
+static hipError_t launch_tiles16(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
+                                 const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
+                                 int64_t ldo, float* fp32_out, hipStream_t s, int mode,
+                                 int splits = 1) {
+    const dim3 grid((unsigned)(((Co + BN - 1) / BN) * ((T + BM - 1) / BM) * splits));
+    const int64_t Kp = round_up_k(Ci);
+    if (fp32_out == nullptr) {
+        hipLaunchKernelGGL((gemm16_kernel<BM, BN, WM, WN, true>), grid, dim3(WM * WN * 64), 0, s,
+                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out, ldo, mode, 1);
+    } else {
+        hipLaunchKernelGGL((gemm16_kernel<BM, BN, WM, WN, false>), grid, dim3(WM * WN * 64), 0, s,
+                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)fp32_out, Co, 0, splits);
+    }
+    return hipGetLastError();
+}
+
 #ifndef TILE_COST_256x128
 #define TILE_COST_256x128 0.69
 #endif
@@ -809,13 +1169,13 @@ static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, c
     // the 32-column grid no longer fits the CUs in one round.
     hipError_t e;
     if (T >= 256 && c224 < c256 && c224 < c192 && c224 < c128)
-        e = launch_tiles<256, 224, 4, 1, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        e = launch_tiles16<256, 224, 4, 1>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T >= 256 && c128 < c256 && c128 <= c192)
-        e = launch_tiles<256, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        e = launch_tiles16<256, 128, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T >= 256 && c192 < c256)
-        e = launch_tiles<192, 256, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        e = launch_tiles16<192, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T >= 256)
-        e = launch_tiles<256, 256, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        e = launch_tiles16<256, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T > 64 || (T > 32 && (Co + 127) / 128 >= kCus))
         e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T > 32 && (Co + 31) / 32 > kCus)
