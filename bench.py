@@ -104,7 +104,7 @@ def traffic_record(fetch_csv, write_csv, workload, copy_mb):
                 if r["Counter_Name"] != counter:
                     continue
                 name = r["Kernel_Name"]
-                key = ("gemm" if "gemm_kernel" in name and "true>" in name
+                key = ("gemm" if "gemm16_kernel<256, 256, 2, 2, true>" in name
                        else "copy" if "copyBuffer" in name else None)
                 if key:
                     vals.setdefault(key, []).append(float(r["Counter_Value"]))
@@ -118,7 +118,7 @@ def traffic_record(fetch_csv, write_csv, workload, copy_mb):
     fetch = f["gemm"] * 1024.0 * f_factor
     write = w["gemm"] * 1024.0 * w_factor
     return {"workload": workload, "gemm_source_sha256_16": gemm_source_hash(),
-            "kernel": "gemm_kernel<..., true> (fused)",
+            "kernel": "gemm16_kernel<256, 256, 2, 2, true> (fused, this workload's tiles)",
             "fetch_kib_raw": f["gemm"], "write_kib_raw": w["gemm"],
             "copy_bytes": copy_bytes, "copy_fetch_kib_raw": f["copy"],
             "copy_write_kib_raw": w["copy"], "fetch_factor": f_factor,
