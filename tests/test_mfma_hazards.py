@@ -1,0 +1,141 @@
+"""Static check of the inline-asm MFMAs in gemm16_kernel (no GPU needed).
+
+gemm16_kernel issues its v_mfma_f32_16x16x128_f8f6f4 from inline asm, which
+the compiler's hazard tracking does not see, so the kernel keeps every
+dependence on an MFMA's registers far apart by construction.  This test
+compiles gemm.hip to gfx950 assembly and checks, for every instantiation, on
+straight-line code and across every loop back edge:
+
+  * after an MFMA writes its accumulator registers, no other instruction
+    touches them within the next 24 wait states (an s_nop N counts N + 1);
+  * before an MFMA, no vector-ALU instruction wrote one of its source or
+    accumulator registers within the previous 6 wait states.
+
+Both windows are several times the wait states a 16x16x128 MFMA needs.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HIPCC = "/opt/rocm/bin/hipcc"
+AFTER_WRITE = 24
+BEFORE_READ = 6
+
+
+def _regs(tok):
+    """Registers named in an operand string, as (kind, index) with kind 'a'
+    (AGPR) or 'v' (VGPR)."""
+    out = set()
+    for m in re.finditer(r"\b([av])\[(\d+):(\d+)\]|\b([av])(\d+)\b", tok):
+        if m.group(4):
+            out.add((m.group(4), int(m.group(5))))
+        else:
+            out.update((m.group(1), r) for r in range(int(m.group(2)), int(m.group(3)) + 1))
+    return out
+
+
+def _wait_states(ins):
+    return int(ins.split()[1]) + 1 if ins.startswith("s_nop") else 1
+
+
+def _functions(asm):
+    for m in re.finditer(r"\n(_ZN4ptpc13gemm16_kernel\w+):", asm):
+        body = asm[m.start():asm.index(".Lfunc_end", m.start())]
+        ins, labels = [], {}
+        for line in body.split("\n")[2:]:
+            line = line.split(";")[0].strip()
+            if not line or (line.startswith(".") and not line.startswith(".LBB")):
+                continue
+            if line.startswith(".LBB"):
+                labels[line.rstrip(":")] = len(ins)
+                continue
+            ins.append(line)
+        yield m.group(1), ins, labels
+
+
+def _sequences(ins, labels):
+    """The straight-line order, plus every loop body followed by its start."""
+    yield list(range(len(ins)))
+    for k, line in enumerate(ins):
+        if line.startswith("s_cbranch") or line.startswith("s_branch"):
+            target = line.split()[-1]
+            if target in labels and labels[target] <= k:
+                start = labels[target]
+                yield list(range(start, k + 1)) + list(range(start, k + 1))
+
+
+def _violations(ins, labels):
+    bad = []
+    for seq in _sequences(ins, labels):
+        for p, k in enumerate(seq):
+            line = ins[k]
+            if not line.startswith("v_mfma"):
+                continue
+            ops = line.split(None, 1)[1].split(", ")
+            dst = _regs(ops[0])
+            waited = 0
+            for q in range(p + 1, len(seq)):
+                other = ins[seq[q]]
+                if waited >= AFTER_WRITE:
+                    break
+                if dst & _regs(other):
+                    bad.append(("after write", line, other, waited))
+                    break
+                waited += _wait_states(other)
+            srcs = set()
+            for op in ops[1:4]:
+                srcs |= _regs(op)
+            waited = 0
+            for q in range(p - 1, -1, -1):
+                other = ins[seq[q]]
+                if waited >= BEFORE_READ:
+                    break
+                if other.startswith("v_") and not other.startswith("v_mfma") \
+                        and not other.startswith("v_cmp"):
+                    d = other.split(None, 1)[1].split(",")[0] if " " in other else ""
+                    written = _regs(d)
+                    if written & srcs:
+                        bad.append(("before read", other, line, waited))
+                        break
+                waited += _wait_states(other)
+    return bad
+
+
+def test_checker_catches_planted_hazards():
+    """The scanner itself: a read of an accumulator right after the MFMA that
+    writes it, a source written just before an MFMA, and the same hazard
+    across a loop back edge are flagged; the spaced-out forms are not."""
+    mfma = "v_mfma_f32_16x16x128_f8f6f4 a[0:3], v[8:15], v[16:23], a[0:3]"
+    assert _violations([mfma, "v_accvgpr_read_b32 v1, a2"], {})
+    assert _violations(["v_mov_b32 v9, 0", mfma], {})
+    assert _violations(["v_accvgpr_write_b32 a1, 0", "s_nop 1", mfma], {})
+    assert not _violations([mfma] + ["s_nop 7"] * 3 + ["v_accvgpr_read_b32 v1, a2"], {})
+    assert not _violations(["v_mov_b32 v9, 0", "s_nop 7", mfma], {})
+    assert not _violations([mfma, "v_mfma_f32_16x16x128_f8f6f4 a[4:7], v[8:15], v[16:23], a[4:7]"], {})
+    loop = ["v_accvgpr_read_b32 v1, a2", "s_nop 7", "s_nop 7", "s_nop 7", mfma,
+            "s_cbranch_scc1 .LBB0_1"]
+    assert not _violations(loop, {})
+    assert _violations(loop, {".LBB0_1": 0})
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_gemm16_inline_mfma_hazards(tmp_path):
+    out = tmp_path / "gemm.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++20", "-ffp-contract=off",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "scaled_gemm_amd", "csrc"),
+           "--cuda-device-only", "-S", "-x", "hip",
+           os.path.join(ROOT, "scaled_gemm_amd", "csrc", "gemm.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+    asm = out.read_text()
+    found = 0
+    for name, ins, labels in _functions(asm):
+        found += 1
+        n_mfma = sum(1 for line in ins if line.startswith("v_mfma"))
+        assert n_mfma > 0, name
+        bad = _violations(ins, labels)
+        assert not bad, (name, bad[:5])
+    assert found >= 8, "expected the fused and two-step forms of four tile shapes"
