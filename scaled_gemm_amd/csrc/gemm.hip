@@ -1176,7 +1176,19 @@ static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, c
         e = launch_tiles16<192, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T >= 256)
         e = launch_tiles16<256, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T > 64 || (T > 32 && (Co + 127) / 128 >= kCus))
+    else if (T > 64) {
+        // 65..255 tokens: the fewest rounds of 256 CUs, and among equal
+        // rounds the smaller tile (more CUs streaming the weight): 128x128
+        // tiles leave most CUs idle on the 8192-column layers.
+        const int64_t r128 = rounds(tiles(128, 128)), r64w = rounds(tiles(64, 128));
+        const int64_t r64 = rounds(tiles(64, 64));
+        if (r64 <= r128 && r64 <= r64w)
+            e = launch_tiles<64, 64, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        else if (r64w <= r128)
+            e = launch_tiles<64, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        else
+            e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+    } else if (T > 32 && (Co + 127) / 128 >= kCus)
         e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T > 32 && (Co + 31) / 32 > kCus)
         e = launch_decode<2, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);

@@ -105,6 +105,8 @@ FULL_CASES = [
     ("ragged", 3, 144, 48),
     ("ragged", 33, 272, 2064),
     ("ragged", 97, 400, 1040),
+    ("ragged", 130, 272, 8208),      # 64x128 tiles (65..255 tokens, fewest rounds)
+    ("ragged", 200, 144, 1040),      # 64x64 tiles, four row tiles
     ("ragged", 48, 272, 10256),
     ("ragged", 20, 144, 32784),
     ("ragged", 24, 208, 8208),
