@@ -314,7 +314,8 @@ def scaled_mm_context(args):
 
 def sweep(args):
     """Per-shape kernel rates over every workload shape (HIP events around each
-    launch on the launch stream, after a warm-up)."""
+    launch on the launch stream, after a warm-up; three interleaved rounds, the
+    best round per stage)."""
     import numpy as np
     import torch
 
@@ -357,18 +358,24 @@ def sweep(args):
             "gemm_tensor": lambda: sg.gemm_tensor(qx, sx_t, pw_t, out=out2),
             "gemm_ws": lambda: sg.gemm_ws(qx, dx, pw, out=out2, workspace=gws),
         }
-        ms = {}
-        for k, fn in calls.items():
+        # Three interleaved rounds over the stages, each stage's best round
+        # reported: a stage timed in one block right after another reads the
+        # clock's settling (short launches by up to 20%).
+        for fn in calls.values():
             for _ in range(max(3, args.warmup)):
                 fn()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-            for i in range(args.steps):
-                ev[2 * i].record(stream)
-                fn()
-                ev[2 * i + 1].record(stream)
-            torch.cuda.synchronize()
-            ms[k] = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1])
-                                   for i in range(args.steps)]))
+        rounds = {k: [] for k in calls}
+        for _ in range(3):
+            for k, fn in calls.items():
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+                for i in range(args.steps):
+                    ev[2 * i].record(stream)
+                    fn()
+                    ev[2 * i + 1].record(stream)
+                torch.cuda.synchronize()
+                rounds[k].append(float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1])
+                                                for i in range(args.steps)])))
+        ms = {k: min(v) for k, v in rounds.items()}
         flops = 2.0 * T * Ci * Co
         act_b = 3.0 * T * Ci + 4.0 * T
         print(json.dumps({
