@@ -509,9 +509,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
 //   16-row slabs (MT MFMAs).  The A fragments of step s+1 are read during
 //   step s (two register sets); the B fragment of slab j is read two slabs
 //   ahead of its use into a ring of three (the last two slabs of step s read
-//   step s+1's first two).  One piece of this side work (an operand read or
-//   a fill) follows each MFMA, so that its issue hides under the running
-//   MFMA.
+//   step s+1's first two).  The pieces of this side work (operand reads and
+//   fills) are spread evenly between the slab's MFMAs, so that their issue
+//   hides under the running MFMAs.
 //   Two barriers per step.  At the top of step s, A of step s+1 has landed
 //   (it is read during step s) and A slot s%2 is free: A of step s+2 is
 //   filled into it.  Before slab NT-2 ("mid"), B of step s+1 has landed (its
@@ -732,7 +732,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
                                          : "+a"(acc[q][j])
                                          : "v"(fr_b[g % RING]), "v"(fr_a[cur][q]));
                         __builtin_amdgcn_sched_barrier(0);
-                        side(std::integral_constant<int, q>{});
+                        // The slab's side items, spread evenly between
+                        // its MFMAs.
+                        if constexpr (NITEM <= MT) {
+                            constexpr int i0 = (q * NITEM + MT - 1) / MT;
+                            constexpr int i1 = ((q + 1) * NITEM + MT - 1) / MT;
+                            [&]<int... Is>(std::integer_sequence<int, Is...>)
+                                __attribute__((always_inline)) {
+                                    (side(std::integral_constant<int, i0 + Is>{}), ...);
+                                }(std::make_integer_sequence<int, i1 - i0>{});
+                        } else {
+                            side(std::integral_constant<int, q>{});
+                        }
                         __builtin_amdgcn_sched_barrier(0);
                     }(), ...);
                 }(std::make_integer_sequence<int, (MT > NITEM ? MT : NITEM)>{});
