@@ -558,8 +558,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
     static_assert(2 * A_PER_W + 2 * B_PER_W < 64, "vmcnt range");
     // B fills of step s+3: the first B1 loads go out in the last two slabs
     // of step s, the other B2 in the first NT-2 slabs of step s+1, after
-    // that step's A fills (NEARLY fills spread over those slabs).
-    constexpr int B1 = (B_PER_W + 1) / 2;
+    // that step's A fills (NEARLY fills spread over those slabs).  B1 makes
+    // the busier of the two windows as light as it can be (fills per slab),
+    // the larger B1 on a tie.
+    constexpr int B1 = [] {
+        int best = B_PER_W, cost = 1 << 30;
+        for (int b = B_PER_W; b >= 1; --b) {
+            const int early = 2 * (A_PER_W + B_PER_W - b), late = b * (NT - 2);
+            const int c = early > late ? early : late;
+            if (c < cost) { cost = c; best = b; }
+        }
+        return best;
+    }();
     constexpr int B2 = B_PER_W - B1;
     constexpr int NEARLY = A_PER_W + B2;
     constexpr int A_SLOT = BM * KS;
