@@ -536,8 +536,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
 //   reads the accumulators only after the loop's final wait and barrier.
 //   Operand registers are only read by the MFMAs (LDS loads may overwrite
 //   them right after issue, as in compiler-scheduled code).
-// The K loop runs whole periods of 6 steps; steps past the data are zero
-// fills.
+// The K loop runs whole periods of 6 steps, then the remaining 0-5 steps,
+// each behind a uniform branch; fills for steps past the data read zeros.
 template <int BM, int BN, int WM, int WN, bool FUSED>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
     const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
@@ -626,12 +626,16 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
     const int a_c16 = ((lane & 7) ^ swz_a(a_r0)) * 16;
     const uint32_t a_lane = (uint32_t)a_r0 * (uint32_t)ldq + (uint32_t)a_c16;
     const uint32_t b_lane = (uint32_t)lane * 16u;
+    // LDS offset of this wave's fills, re-defined at every step (an empty
+    // asm) so that the compiler forms each fill's LDS address with one add
+    // instead of holding one register per fill and slot across the loop.
+    int wlds = wave * 1024;
     auto issue_a = [&](int ks, int p, uint8_t* slot) __attribute__((always_inline)) {
         const int k0 = ks * KS;
         const bool in = (a_r0 + p * NW * 8 < (int)a_rows) & (k0 + a_c16 < k_lim);
         const uint32_t off =
             in ? a_lane + (uint32_t)(p * NW * 8) * (uint32_t)ldq + (uint32_t)k0 : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + (wave + p * NW) * 1024),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + wlds + p * NW * 1024),
                                                  16, off, 0, 0, 0);
     };
     auto issue_b = [&](int ks, int p, uint8_t* slot) __attribute__((always_inline)) {
@@ -641,8 +645,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
         const uint32_t off =
             in ? b_lane + ((uint32_t)(blk * 16) * (uint32_t)Kp + (uint32_t)(h * 1024 + ks * 2048))
                : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + bl * 1024), 16, off, 0,
-                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + wlds + p * NW * 1024), 16,
+                                                 off, 0, 0, 0);
     };
 
     // Operand reads (see the layout above); the swizzle of a 16-row slab
@@ -686,6 +690,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
     // its side work threaded between them (see above).
     auto step = [&](auto U, int s) __attribute__((always_inline)) {
         constexpr int u = decltype(U)::value;
+        asm volatile("" : "+s"(wlds));
         constexpr int cur = u & 1;
         const uint8_t* const na = a_slot((u + 1) % 2);
         const uint8_t* const cb = b_slot(u % 3);
@@ -789,13 +794,24 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
         fr_b[0] = read_b(b_s0, 0);
         fr_b[1] = read_b(b_s0, 1);
         constexpr int P = 6;
-        for (int s0 = 0; s0 < nsteps; s0 += P) {
+        int s0 = 0;
+        for (; s0 + P <= nsteps; s0 += P) {
             [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
                 ((sync(std::integral_constant<int, B_PER_W>{}),
                   step(std::integral_constant<int, Us>{}, s0 + Us)),
                  ...);
             }(std::make_integer_sequence<int, P>{});
         }
+        const int rem = __builtin_amdgcn_readfirstlane(nsteps - s0);
+        [&]<int... Us>(std::integer_sequence<int, Us...>) __attribute__((always_inline)) {
+            (([&]() __attribute__((always_inline)) {
+                 if (Us < rem) {
+                     sync(std::integral_constant<int, B_PER_W>{});
+                     step(std::integral_constant<int, Us>{}, s0 + Us);
+                 }
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, P - 1>{});
         wait_counts<0, 0>();
         lds_barrier();
     }

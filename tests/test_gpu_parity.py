@@ -114,6 +114,11 @@ FULL_CASES = [
     ("ragged", 513, 512, 2064),
     ("ragged", 600, 144, 22000),
     ("ragged", 500, 144, 28656),
+    # 128-byte K steps run in periods of 6, the rest one by one: 12, 7 and 11
+    # steps (remainders 0, 1 and 5; the cases above cover 2, 3 and 4)
+    ("ragged", 280, 1536, 528),
+    ("ragged", 272, 880, 1296),
+    ("ragged", 520, 1392, 400),
 ]
 
 
@@ -129,19 +134,27 @@ def test_full_parity_other_seeds(name, seed):
     assert np.array_equal(g["out"], g["out2"]), "fused and two-step differ"
 
 
+def ragged_inputs(T, Ci, Co):
+    """Seeded inputs of any shape: N(0,1) activations with every (Ci/7)-th
+    channel scaled by 60 and a zero row, N(0, 0.02^2) weights with a zero
+    column."""
+    rng = np.random.default_rng(T * 7 + Ci)
+    x = workloads.random_bf16(rng, T, Ci, 1.0)
+    x[:, :: max(1, Ci // 7)] = workloads.f32_to_bf16_bits(
+        workloads.bf16_bits_to_f32(x[:, :: max(1, Ci // 7)]) * np.float32(60))
+    if T > 2:
+        x[1] = 0
+    w = workloads.random_bf16(rng, Ci, Co, 0.02)
+    if Co > 16:
+        w[:, 5] = 0
+    return x, w
+
+
 @pytest.mark.parametrize("name,T,Ci,Co", FULL_CASES)
 def test_full_parity(name, T, Ci, Co):
     note(f"full parity {name} T={T} Ci={Ci} Co={Co}")
     if name == "ragged":
-        rng = np.random.default_rng(T * 7 + Ci)
-        x = workloads.random_bf16(rng, T, Ci, 1.0)
-        x[:, :: max(1, Ci // 7)] = workloads.f32_to_bf16_bits(
-            workloads.bf16_bits_to_f32(x[:, :: max(1, Ci // 7)]) * np.float32(60))
-        if T > 2:
-            x[1] = 0
-        w = workloads.random_bf16(rng, Ci, Co, 0.02)
-        if Co > 16:
-            w[:, 5] = 0
+        x, w = ragged_inputs(T, Ci, Co)
     else:
         _, x, w = workloads.make(name)
     g = run_path(x, w)
@@ -166,6 +179,23 @@ def sampled_case(x, w, what, seed):
     assert np.array_equal(g["out"], g["out2"]), f"{what}: fused and two-step differ"
     check_bf16_two_step(g, ref, what, rows, cols)
     return g
+
+
+# The small cases above all get 256x128 tiles; these shapes select each of
+# the other tile shapes of the 128-byte-step kernel, with K remainders the
+# full-size configs do not have (ragged K, periods of 6 steps plus 1, 5, 0).
+TILE_CASES = [
+    (4096, 1648, 4096),     # 256x256 tiles, 13 K steps
+    (1024, 592, 10240),     # 192x256 tiles, 5 K steps
+    (1024, 752, 14336),     # 256x224 tiles, 6 K steps
+]
+
+
+@pytest.mark.parametrize("T,Ci,Co", TILE_CASES)
+def test_tile_shape_parity(T, Ci, Co):
+    note(f"tile-shape parity T={T} Ci={Ci} Co={Co}")
+    x, w = ragged_inputs(T, Ci, Co)
+    sampled_case(x, w, f"T={T} Ci={Ci} Co={Co}", seed=T + Ci)
 
 
 @pytest.mark.parametrize("name", ["8b_gate_up", "70b_down"])

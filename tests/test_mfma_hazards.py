@@ -4,7 +4,8 @@ gemm16_kernel issues its v_mfma_f32_16x16x128_f8f6f4 from inline asm, which
 the compiler's hazard tracking does not see, so the kernel keeps every
 dependence on an MFMA's registers far apart by construction.  This test
 compiles gemm.hip to gfx950 assembly and checks, for every instantiation, on
-straight-line code and across every loop back edge:
+straight-line code, across every loop back edge and along every forward
+branch:
 
   * after an MFMA writes its accumulator registers, no other instruction
     touches them within the next 24 wait states (an s_nop N counts N + 1);
@@ -57,7 +58,8 @@ def _functions(asm):
 
 
 def _sequences(ins, labels):
-    """The straight-line order, plus every loop body followed by its start."""
+    """The straight-line order, every loop body followed by its start, and
+    every forward branch taken (the code before it, then its target)."""
     yield list(range(len(ins)))
     for k, line in enumerate(ins):
         if line.startswith("s_cbranch") or line.startswith("s_branch"):
@@ -65,6 +67,9 @@ def _sequences(ins, labels):
             if target in labels and labels[target] <= k:
                 start = labels[target]
                 yield list(range(start, k + 1)) + list(range(start, k + 1))
+            elif target in labels:
+                t = labels[target]
+                yield list(range(max(0, k - 64), k + 1)) + list(range(t, min(len(ins), t + 64)))
 
 
 def _violations(ins, labels):
@@ -119,6 +124,10 @@ def test_checker_catches_planted_hazards():
             "s_cbranch_scc1 .LBB0_1"]
     assert not _violations(loop, {})
     assert _violations(loop, {".LBB0_1": 0})
+    skip = [mfma, "s_cbranch_scc1 .LBB0_2", "s_nop 7", "s_nop 7", "s_nop 7",
+            "v_accvgpr_read_b32 v1, a3"]
+    assert not _violations(skip, {})
+    assert _violations(skip, {".LBB0_2": 5})
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
