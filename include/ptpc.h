@@ -125,7 +125,10 @@ ptpc_status ptpc_gemm(const uint8_t* qx, int64_t ldq, const float* dx,
 /*
  * Workspace that lets ptpc_gemm_ws split K across workgroups: nonzero only
  * for token counts whose output tiles are too few to occupy the GPU (65..255
- * tokens with few output columns), then 4 * S * T * Co bytes for S K ranges.
+ * tokens with few output columns, except where ptpc_gemm already splits K
+ * inside each workgroup of 64x64 tiles: up to 128 tokens when those tiles
+ * need no more rounds of the GPU than larger ones), then 4 * S * T * Co
+ * bytes for S K ranges.
  */
 size_t ptpc_gemm_workspace_bytes(int64_t T, int64_t Ci, int64_t Co);
 

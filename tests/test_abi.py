@@ -120,16 +120,17 @@ def test_gemm_validation(L):
     assert L.ptpc_gemm_unfused_bf16(A, 256, B, C, D, 4, 256, 512, E, 512, MIS, None) == 4
     assert L.ptpc_gemm_unfused_bf16(A, 256, B, C, D, 4, 256, 500, E, 512, D, None) == 3
     assert L.ptpc_gemm_unfused_bf16_workspace_bytes(3, 16) == 3 * 16 * 2
-    # split-K workspace: 128 tokens x 8192 -> 8192 columns splits K four ways
-    need = L.ptpc_gemm_workspace_bytes(128, 8192, 8192)
-    assert need == 4 * 4 * 128 * 8192
+    # split-K workspace: 128 tokens x 8192 -> 10240 columns splits K three ways
+    need = L.ptpc_gemm_workspace_bytes(128, 8192, 10240)
+    assert need == 3 * 4 * 128 * 10240
     assert L.ptpc_gemm_workspace_bytes(4096, 28672, 8192) == 0          # enough tiles
     assert L.ptpc_gemm_workspace_bytes(16, 8192, 8192) == 0             # few-token kernel
     assert L.ptpc_gemm_workspace_bytes(128, 8192, 57344) == 0           # 448 tiles
+    assert L.ptpc_gemm_workspace_bytes(128, 8192, 8192) == 0            # K split in-workgroup
     g = L.ptpc_gemm_ws
-    assert g(A, 8192, B, C, D, 128, 8192, 8192, E, 8192, NULL, 0, None) == 1
-    assert g(A, 8192, B, C, D, 128, 8192, 8192, E, 8192, D, need - 16, None) == 2
-    assert g(A, 8192, B, C, D, 128, 8192, 8192, E, 8192, MIS, need, None) == 4
+    assert g(A, 8192, B, C, D, 128, 8192, 10240, E, 10240, NULL, 0, None) == 1
+    assert g(A, 8192, B, C, D, 128, 8192, 10240, E, 10240, D, need - 16, None) == 2
+    assert g(A, 8192, B, C, D, 128, 8192, 10240, E, 10240, MIS, need, None) == 4
     assert g(A, 256, B, C, D, 4, 256, 500, E, 512, D, 0, None) == 3
     assert L.ptpc_gemm_unfused(A, 256, B, C, D, 4, 256, 512, E, 512, MIS, None) == 4
 
@@ -182,7 +183,7 @@ r = [L.ptpc_quant_act(A, 4, 256, 256, B, 256, C, None),
      L.ptpc_quant_weight_static(A, 256, 512, 512, B, C, None),
      L.ptpc_gemm_tensor(A, 256, B, C, D, 4, 256, 512, E, 512, None),
      L.ptpc_gemm_unfused_bf16(A, 256, B, C, D, 4, 256, 512, E, 512, D, None),
-     L.ptpc_gemm_ws(A, 8192, B, C, D, 128, 8192, 8192, E, 8192, D, 1 << 30, None),
+     L.ptpc_gemm_ws(A, 8192, B, C, D, 128, 8192, 10240, E, 10240, D, 1 << 30, None),
      L.ptpc_quant_act(A, 0, 256, 256, B, 256, C, None)]
 print(r)
 assert r == [5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 0], r

@@ -119,6 +119,11 @@ FULL_CASES = [
     ("ragged", 280, 1536, 528),
     ("ragged", 272, 880, 1296),
     ("ragged", 520, 1392, 400),
+    # 65..128 tokens on 64x64 tiles: K steps dealt to 4 waves (1 step: three
+    # waves idle; 13 and 27 steps: uneven counts per wave)
+    ("ragged", 100, 16, 2064),
+    ("ragged", 65, 1552, 528),
+    ("ragged", 120, 3344, 1040),
 ]
 
 
@@ -388,7 +393,7 @@ def test_gemm_ws_split_k_ragged():
     """K cut into ranges (here 4, the last one holding the K tail), rows and
     columns ragged: whole output against the oracle, deterministic across
     calls, and the workspace contents do not matter."""
-    T, Ci, Co = 100, 4112, 400
+    T, Ci, Co = 200, 4112, 400
     need = sg.gemm_workspace_bytes(T, Ci, Co)
     assert need == 4 * 4 * T * Co
     rng = np.random.default_rng(31)
@@ -408,8 +413,9 @@ def test_gemm_ws_split_k_ragged():
 
 
 def test_gemm_ws_sweep_t128():
-    """The 70B layers at 128 tokens through ptpc_gemm_ws (QKV: 3 K ranges,
-    O and down: 4, gate_up: no split -> bit-identical to ptpc_gemm)."""
+    """The 70B layers at 128 tokens through ptpc_gemm_ws (QKV: 3 K ranges;
+    O and down, whose 64x64 tiles split K inside the workgroup, and gate_up:
+    no split -> bit-identical to ptpc_gemm)."""
     for layer in workloads.SWEEP_LAYERS:
         shape, x, w = workloads.make("70b_sweep", T=128, layer=layer)
         note(f"split-K 70b {layer} T=128")

@@ -1,7 +1,8 @@
-"""Static check of the inline-asm MFMAs in gemm16_kernel (no GPU needed).
+"""Static check of the inline-asm MFMAs in gemm16_kernel and gemm16s_kernel
+(no GPU needed).
 
-gemm16_kernel issues its v_mfma_f32_16x16x128_f8f6f4 from inline asm, which
-the compiler's hazard tracking does not see, so the kernel keeps every
+Both kernels issue their v_mfma_f32_16x16x128_f8f6f4 from inline asm, which
+the compiler's hazard tracking does not see, so the kernels keep every
 dependence on an MFMA's registers far apart by construction.  This test
 compiles gemm.hip to gfx950 assembly and checks, for every instantiation, on
 straight-line code, across every loop back edge and along every forward
@@ -43,7 +44,7 @@ def _wait_states(ins):
 
 
 def _functions(asm):
-    for m in re.finditer(r"\n(_ZN4ptpc13gemm16_kernel\w+):", asm):
+    for m in re.finditer(r"\n(_ZN4ptpc1[34]gemm16s?_kernel\w+):", asm):
         body = asm[m.start():asm.index(".Lfunc_end", m.start())]
         ins, labels = [], {}
         for line in body.split("\n")[2:]:
@@ -147,4 +148,4 @@ def test_gemm16_inline_mfma_hazards(tmp_path):
         assert n_mfma > 0, name
         bad = _violations(ins, labels)
         assert not bad, (name, bad[:5])
-    assert found >= 8, "expected the fused and two-step forms of four tile shapes"
+    assert found >= 10, "expected the fused and two-step forms of five kernels"
