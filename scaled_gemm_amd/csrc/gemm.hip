@@ -1586,8 +1586,8 @@ static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, c
             e = launch_tiles<64, 64, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
         else if (r64w <= r128)
             e = launch_tiles<64, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-        else
-            e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        else   // 128x128 tiles: the 16x16x128 kernel, 3-5% faster here (70B gate_up)
+            e = launch_tiles16<128, 128, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     } else if (T > 32 && (Co + 127) / 128 >= kCus)
         e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T > 32 && (Co + 31) / 32 > kCus)

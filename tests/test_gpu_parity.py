@@ -124,6 +124,7 @@ FULL_CASES = [
     ("ragged", 100, 16, 2064),
     ("ragged", 65, 1552, 528),
     ("ragged", 120, 3344, 1040),
+    ("ragged", 200, 272, 36864),     # 128x128 tiles of the 16x16x128 kernel at 65..255 tokens
 ]
 
 
