@@ -189,10 +189,11 @@ def sampled_case(x, w, what, seed):
 
 # The small cases above all get 256x128 tiles; these shapes select each of
 # the other tile shapes of the 128-byte-step kernel, with K remainders the
-# full-size configs do not have (ragged K, periods of 6 steps plus 1, 5, 0).
+# full-size configs do not have (ragged K, periods of 6 steps plus 1, 5, 0, 1).
 TILE_CASES = [
     (4096, 1648, 4096),     # 256x256 tiles, 13 K steps
-    (1024, 592, 10240),     # 192x256 tiles, 5 K steps
+    (1536, 592, 8192),      # 192x256 tiles, 5 K steps
+    (1024, 880, 10240),     # 256x160 tiles, 7 K steps
     (1024, 752, 14336),     # 256x224 tiles, 6 K steps
 ]
 
