@@ -1522,6 +1522,9 @@ static hipError_t launch_tiles16s(const uint8_t* qx, int64_t ldq, const float* d
 #ifndef TILE_COST_256x224
 #define TILE_COST_256x224 0.92
 #endif
+#ifndef TILE_COST_128x128
+#define TILE_COST_128x128 0.55
+#endif
 #ifndef TILE_COST_256x160
 #define TILE_COST_256x160 0.83
 #endif
@@ -1544,10 +1547,12 @@ static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, c
                        int64_t ldo, float* fp32_out, hipStream_t s, int ts) {
     // Tile choice: 256x256 keeps the most MFMA work per loaded byte; when it
     // leaves CUs idle or a badly filled last round, 256x224 (4 waves side by
-    // side along the tokens), 192x256, 256x160 or 256x128 -- more tiles, each
-    // costing 0.92, 0.88, 0.83 or 0.69 of a 256x256 one, measured on the 8B /
-    // 70B layers -- is taken if its rounds cost less (256x160: the 70B QKV
-    // layer at 1024 tokens, 256 tiles for 256 CUs, 6% faster than 192x256).
+    // side along the tokens), 192x256, 256x160, 256x128 or 128x128 -- more
+    // tiles, each costing 0.92, 0.88, 0.83, 0.69 or 0.55 of a 256x256 one,
+    // measured on the 8B / 70B layers -- is taken if its rounds cost less
+    // (256x160: the 70B QKV layer at 1024 tokens, 256 tiles for 256 CUs, 6%
+    // faster than 192x256; 128x128: 256..600 tokens of the 8192-column
+    // layers, where 256-row tiles leave CUs idle, 18-29% faster).
     auto rounds = [](int64_t tiles) { return (tiles + kCus - 1) / kCus; };
     auto tiles = [&](int64_t bm, int64_t bn) { return ((T + bm - 1) / bm) * ((Co + bn - 1) / bn); };
     // Cost in 256x256 tile-times of each tiled form: rounds of 256 CUs times
@@ -1566,7 +1571,11 @@ static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, c
     // the 32-column grid no longer fits the CUs in one round.
     hipError_t e;
     const double c160 = TILE_COST_256x160 * (double)rounds(tiles(256, 160));
-    if (T >= 256 && c160 < c256 && c160 < c192 && c160 < c128 && c160 < c224)
+    const double c1616 = TILE_COST_128x128 * (double)rounds(tiles(128, 128));
+    if (T >= 256 && c1616 < c256 && c1616 < c128 && c1616 < c192 && c1616 < c160 &&
+        c1616 < c224)
+        e = launch_tiles16<128, 128, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+    else if (T >= 256 && c160 < c256 && c160 < c192 && c160 < c128 && c160 < c224)
         e = launch_tiles16<256, 160, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
     else if (T >= 256 && c224 < c256 && c224 < c192 && c224 < c128)
         e = launch_tiles16<256, 224, 4, 1>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
