@@ -8,7 +8,7 @@
 //
 // out[t,o] = bf16((acc[t,o] * dx[t]) * dw[o]),
 // acc[t,o] = sum_k qx[t,k] * qw[k,o] on OCP E4M3 values, fp32 accumulation
-// in v_mfma_f32_16x16x128_f8f6f4 (256-token tiles) or
+// in v_mfma_f32_16x16x128_f8f6f4 (gemm16_kernel, gemm16s_kernel) or
 // v_mfma_f32_32x32x64_f8f6f4 (the other kernels).
 //
 // Data layout: qx is [T x Ci] row-major (K contiguous).  The packed weight
@@ -31,11 +31,13 @@
 // fills 1 KB of LDS (64 lanes x 16 B), each lane fetching the global chunk
 // that belongs in its fixed LDS slot.
 //
-// Kernels: gemm16_kernel (tiled, 192..256-token x 128..256-column tiles,
-// 16x16x128 MFMAs), gemm_kernel (tiled, 32x64 and 128x128 tiles and the
-// split-K form, 32x32x64 MFMAs), gemm_decode_kernel (up to 64 tokens: K split
-// across the waves of a workgroup), and the second passes of the two-step
-// forms and of split-K.
+// Kernels: gemm16_kernel (tiled, 128..256-row x 128..256-column tiles,
+// 16x16x128 MFMAs), gemm16s_kernel (64x64 tiles of 65..128 tokens, the K
+// steps split between the waves, each on its own LDS ring), gemm_kernel
+// (tiled, 32x64 and 64-row tiles and the split-K form, 32x32x64 MFMAs),
+// gemm_decode_kernel (up to 64 tokens: K split across the waves of a
+// workgroup, operands loaded straight into registers), and the second
+// passes of the two-step forms and of split-K.
 #include <utility>
 
 #include "device_common.h"
