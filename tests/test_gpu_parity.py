@@ -334,10 +334,12 @@ def test_empty_and_zero_extents():
     assert sg.gemm(q1, d1, pw1).shape == (3, 0)
 
 
-def test_pitched_inputs_and_outputs():
-    """Row pitches larger than the extents (views into wider buffers)."""
+@pytest.mark.parametrize("T", [70, 300])
+def test_pitched_inputs_and_outputs(T):
+    """Row pitches larger than the extents (views into wider buffers); 70
+    tokens run the K-split 64x64 tiles, 300 the 128-byte-step tiled kernel."""
     rng = np.random.default_rng(12)
-    T, Ci, Co = 70, 528, 208
+    Ci, Co = 528, 208
     xb = workloads.random_bf16(rng, T, Ci + 40, 1.0)
     wb = workloads.random_bf16(rng, Ci, Co + 24, 0.02)
     xd = bits_to_dev(xb)[:, :Ci]
