@@ -335,10 +335,10 @@ hipError_t launch_quant_weight(const uint16_t* w, int64_t Ci, int64_t Co, int64_
                        amax_bits, Co);
     if (Ci > 0) {
         const int64_t colblocks = (Co + kColsPerBlock - 1) / kColsPerBlock;
-        // About 512 workgroups in all (2 per CU): fewer, longer row splits
-        // than 2048 were 4-10% faster over the whole weight quantization
-        // (fewer atomics per column, less tail).
-        int64_t splits = 512 / colblocks;
+        // About 256 workgroups in all (one per CU): fewer, longer row splits
+        // than 2048 were 6-12% faster over the whole weight quantization
+        // (fewer atomics per column, less tail); 128 was slower again.
+        int64_t splits = 256 / colblocks;
         if (splits < 1) splits = 1;
         int64_t max_splits = (Ci + 31) / 32;    // at least 32 rows per split
         if (splits > max_splits) splits = max_splits;
