@@ -313,9 +313,10 @@ def scaled_mm_context(args):
 
 
 def sweep(args):
-    """Per-shape kernel rates over every workload shape (HIP events around each
-    launch on the launch stream, after a warm-up; three interleaved rounds, the
-    best round per stage)."""
+    """Per-shape kernel rates over every workload shape (after a warm-up, three
+    interleaved rounds over the stages, each round one HIP event pair on the
+    launch stream around `steps` back-to-back launches; the best round per
+    stage)."""
     import numpy as np
     import torch
 
@@ -367,14 +368,13 @@ def sweep(args):
         rounds = {k: [] for k in calls}
         for _ in range(3):
             for k, fn in calls.items():
-                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                ev[0].record(stream)
                 for i in range(args.steps):
-                    ev[2 * i].record(stream)
                     fn()
-                    ev[2 * i + 1].record(stream)
+                ev[1].record(stream)
                 torch.cuda.synchronize()
-                rounds[k].append(float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1])
-                                                for i in range(args.steps)])))
+                rounds[k].append(ev[0].elapsed_time(ev[1]) / args.steps)
         ms = {k: min(v) for k, v in rounds.items()}
         flops = 2.0 * T * Ci * Co
         act_b = 3.0 * T * Ci + 4.0 * T
