@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--model-load", action="store_true",
                    help="quantize + prepack every linear weight of the 80 Llama-3.1-70B "
                         "decoder layers and report the load-time cost (one JSON line)")
+    p.add_argument("--mfma-ceiling", action="store_true",
+                   help="register-only FP8 MFMA throughput of the whole chip in the two MFMA "
+                        "forms the GEMM uses (the power-limited ceiling; one JSON line)")
     p.add_argument("--sweep", action="store_true",
                    help="one JSON line per workload shape (every config, every 70B layer x T): "
                         "quant_act GB/s, fused / two-step GEMM TFLOP/s; not the bench line")
@@ -312,6 +315,49 @@ def scaled_mm_context(args):
     }), flush=True)
 
 
+def mfma_ceiling(args):
+    """Register-only FP8 MFMA throughput: one workgroup of 4 waves per CU,
+    random finite E4M3 operands in registers, a 128x128 fp32 accumulator per
+    wave, no memory traffic; ~100 ms per launch, so that the chip's
+    sustained power limit sets the clock."""
+    import ctypes
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "scaled_gemm_amd", "libmfma_probe.so"))
+    lib.mfma_peak.restype = ctypes.c_int
+    lib.mfma_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p,
+                              ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    blocks = 256
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {}
+    # per iteration a wave updates its 128x128 accumulator over K = 128
+    # (64 MFMAs of 16x16x128) or K = 64 (16 MFMAs of 32x32x64)
+    for form, name, iters, k in ((16, "16x16x128", 100000, 128), (32, "32x32x64", 200000, 64)):
+        flops = blocks * 4 * iters * 2.0 * 128 * 128 * k
+        def run():
+            assert lib.mfma_peak(form, blocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                 ctypes.c_void_p(stream.cuda_stream)) == 0
+        run()
+        torch.cuda.synchronize()
+        rates = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rates.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        res[name] = {"tflops": [round(r, 1) for r in rates],
+                     "frac_of_peak": round(max(rates) / PEAK_FP8_TFLOPS, 4),
+                     "ms_per_launch": round(flops / max(rates) / 1e9, 2)}
+    print(json.dumps({"what": "register-only FP8 MFMA throughput (no memory traffic), "
+                              "256 CUs x 4 waves, 128x128 fp32 accumulator per wave",
+                      "peak_tflops": PEAK_FP8_TFLOPS, "forms": res}), flush=True)
+
+
 def sweep(args):
     """Per-shape kernel rates over every workload shape (after a warm-up, three
     interleaved rounds over the stages, each round one HIP event pair on the
@@ -402,6 +448,9 @@ def sweep(args):
 
 def main():
     args = parse()
+    if args.mfma_ceiling:
+        mfma_ceiling(args)
+        return
     if args.sweep:
         sweep(args)
         return

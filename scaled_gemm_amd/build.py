@@ -16,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libptpc.so")
+PROBE_LIB = os.path.join(PKG, "libmfma_probe.so")
 
 SOURCES = ["ptpc_api.cpp", "quant.hip", "gemm.hip"]
 
@@ -56,6 +57,12 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    # The register-only MFMA throughput probe behind `bench.py --mfma-ceiling`:
+    # its own shared object, not part of the library.
+    ptmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, *FLAGS, *extra_flags, "-x", "hip", "-shared", "-o", ptmp,
+          os.path.join(PKG, "probe", "mfma_peak.hip")], verbose)
+    os.replace(ptmp, PROBE_LIB)
     return LIB
 
 
