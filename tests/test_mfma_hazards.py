@@ -149,3 +149,30 @@ def test_gemm16_inline_mfma_hazards(tmp_path):
         bad = _violations(ins, labels)
         assert not bad, (name, bad[:5])
     assert found >= 10, "expected the fused and two-step forms of five kernels"
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_mfma_probe_inline_hazards(tmp_path):
+    """The register-only ceiling probe issues its 16x16x128 MFMAs from inline
+    asm too; scan that instantiation the same way."""
+    out = tmp_path / "probe.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++20", "-ffp-contract=off",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "--cuda-device-only", "-S", "-x", "hip",
+           os.path.join(ROOT, "scaled_gemm_amd", "probe", "mfma_peak.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+    asm = out.read_text()
+    m = re.search(r"\n(_ZN\w*mfma_peak_kernelILi16E\w*):", asm)
+    assert m, "16x16x128 probe kernel not found"
+    body = asm[m.start():asm.index(".Lfunc_end", m.start())]
+    ins, labels = [], {}
+    for line in body.split("\n")[2:]:
+        line = line.split(";")[0].strip()
+        if not line or (line.startswith(".") and not line.startswith(".LBB")):
+            continue
+        if line.startswith(".LBB"):
+            labels[line.rstrip(":")] = len(ins)
+            continue
+        ins.append(line)
+    assert sum(1 for line in ins if line.startswith("v_mfma")) == 64
+    assert not _violations(ins, labels)
