@@ -73,7 +73,8 @@ def check_per_tensor_quant(g, x_bits, w_bits, what):
 
 
 CASES = [("tiny", 16, 256, 512), ("ragged", 48, 272, 10256), ("ragged", 300, 1040, 784),
-         ("ragged", 1, 16, 16), ("8b_qkv_decode", 32, 4096, 6144)]
+         ("ragged", 1, 16, 16), ("8b_qkv_decode", 32, 4096, 6144),
+         ("ragged", 100, 528, 1040)]      # the K-split 64x64 tiles with scalar scales
 
 
 @pytest.mark.parametrize("name,T,Ci,Co", CASES)
