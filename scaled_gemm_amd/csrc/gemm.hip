@@ -436,10 +436,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
                         const float sx = sxv[i];
                         const float4 sw = swv[j][g];
                         uint2 pk;
-                        pk.x = (uint32_t)f32_to_bf16_rne((acc[i][j][4 * g + 0] * sx) * sw.x) |
-                               ((uint32_t)f32_to_bf16_rne((acc[i][j][4 * g + 1] * sx) * sw.y) << 16);
-                        pk.y = (uint32_t)f32_to_bf16_rne((acc[i][j][4 * g + 2] * sx) * sw.z) |
-                               ((uint32_t)f32_to_bf16_rne((acc[i][j][4 * g + 3] * sx) * sw.w) << 16);
+                        pk.x = f32x2_to_bf16x2_rne((acc[i][j][4 * g + 0] * sx) * sw.x,
+                               (acc[i][j][4 * g + 1] * sx) * sw.y);
+                        pk.y = f32x2_to_bf16x2_rne((acc[i][j][4 * g + 2] * sx) * sw.z,
+                               (acc[i][j][4 * g + 3] * sx) * sw.w);
                         *reinterpret_cast<uint2*>(stage + lr * PITCH +
                                                   (slot_of(lr, 4 * j + g) << 4) + lg * 8) = pk;
                     }
@@ -858,10 +858,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
                 const float sx = sxv[i];
                 const float4 sw = swv[j];
                 uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16_rne((acc[i][j][0] * sx) * sw.x) |
-                       ((uint32_t)f32_to_bf16_rne((acc[i][j][1] * sx) * sw.y) << 16);
-                pk.y = (uint32_t)f32_to_bf16_rne((acc[i][j][2] * sx) * sw.z) |
-                       ((uint32_t)f32_to_bf16_rne((acc[i][j][3] * sx) * sw.w) << 16);
+                pk.x = f32x2_to_bf16x2_rne((acc[i][j][0] * sx) * sw.x,
+                       (acc[i][j][1] * sx) * sw.y);
+                pk.y = f32x2_to_bf16x2_rne((acc[i][j][2] * sx) * sw.z,
+                       (acc[i][j][3] * sx) * sw.w);
                 *reinterpret_cast<uint2*>(stage + l16 * PITCH +
                                           (slot_of(l16, 2 * j + (lg >> 1)) << 4) +
                                           (lg & 1) * 8) = pk;
@@ -1167,10 +1167,10 @@ __global__ __launch_bounds__(256, 1) void gemm16s_kernel(
             const float4 sw = col < Co ? scale_of_cols(dw, col, scale_mode)
                                        : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
             uint2 pk;
-            pk.x = (uint32_t)f32_to_bf16_rne((sum[j][0] * sx) * sw.x) |
-                   ((uint32_t)f32_to_bf16_rne((sum[j][1] * sx) * sw.y) << 16);
-            pk.y = (uint32_t)f32_to_bf16_rne((sum[j][2] * sx) * sw.z) |
-                   ((uint32_t)f32_to_bf16_rne((sum[j][3] * sx) * sw.w) << 16);
+            pk.x = f32x2_to_bf16x2_rne((sum[j][0] * sx) * sw.x,
+                   (sum[j][1] * sx) * sw.y);
+            pk.y = f32x2_to_bf16x2_rne((sum[j][2] * sx) * sw.z,
+                   (sum[j][3] * sx) * sw.w);
             *reinterpret_cast<uint2*>(stage + l16 * PITCH + (slot_of(l16, 2 * j + (lg >> 1)) << 4) +
                                       (lg & 1) * 8) = pk;
         }
@@ -1353,10 +1353,10 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_decode_kernel(
             const float sx = sxp[k];
             const float4 sw = swp[k];
             uint2 pk;
-            pk.x = (uint32_t)f32_to_bf16_rne((v[0] * sx) * sw.x) |
-                   ((uint32_t)f32_to_bf16_rne((v[1] * sx) * sw.y) << 16);
-            pk.y = (uint32_t)f32_to_bf16_rne((v[2] * sx) * sw.z) |
-                   ((uint32_t)f32_to_bf16_rne((v[3] * sx) * sw.w) << 16);
+            pk.x = f32x2_to_bf16x2_rne((v[0] * sx) * sw.x,
+                   (v[1] * sx) * sw.y);
+            pk.y = f32x2_to_bf16x2_rne((v[2] * sx) * sw.z,
+                   (v[3] * sx) * sw.w);
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + row * ldo + c) = pk;
         } else {
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + row * Co + c) =
@@ -1399,10 +1399,10 @@ __global__ __launch_bounds__(256) void rescale_kernel(const float* __restrict__ 
         const float4 s = *reinterpret_cast<const float4*>(dw + o);
         const float st = dx[t];
         uint2 packed;
-        packed.x = (uint32_t)f32_to_bf16_rne((a.x * st) * s.x) |
-                   ((uint32_t)f32_to_bf16_rne((a.y * st) * s.y) << 16);
-        packed.y = (uint32_t)f32_to_bf16_rne((a.z * st) * s.z) |
-                   ((uint32_t)f32_to_bf16_rne((a.w * st) * s.w) << 16);
+        packed.x = f32x2_to_bf16x2_rne((a.x * st) * s.x,
+                   (a.y * st) * s.y);
+        packed.y = f32x2_to_bf16x2_rne((a.z * st) * s.z,
+                   (a.w * st) * s.w);
         *reinterpret_cast<uint2*>(out + t * ldo + o) = packed;
     }
 }
@@ -1425,10 +1425,10 @@ __global__ __launch_bounds__(256) void rescale_bf16_kernel(const uint16_t* __res
         const float4 sc = *reinterpret_cast<const float4*>(dw + o);
         const float st = dx[t];
         uint2 packed;
-        packed.x = (uint32_t)f32_to_bf16_rne((bf16lo_to_f32(a.x) * st) * sc.x) |
-                   ((uint32_t)f32_to_bf16_rne((bf16hi_to_f32(a.x) * st) * sc.y) << 16);
-        packed.y = (uint32_t)f32_to_bf16_rne((bf16lo_to_f32(a.y) * st) * sc.z) |
-                   ((uint32_t)f32_to_bf16_rne((bf16hi_to_f32(a.y) * st) * sc.w) << 16);
+        packed.x = f32x2_to_bf16x2_rne((bf16lo_to_f32(a.x) * st) * sc.x,
+                   (bf16hi_to_f32(a.x) * st) * sc.y);
+        packed.y = f32x2_to_bf16x2_rne((bf16lo_to_f32(a.y) * st) * sc.z,
+                   (bf16hi_to_f32(a.y) * st) * sc.w);
         *reinterpret_cast<uint2*>(out + t * ldo + o) = packed;
     }
 }
@@ -1460,10 +1460,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         const float4 sc = *reinterpret_cast<const float4*>(dw + o);
         const float st = dx[t];
         uint2 packed;
-        packed.x = (uint32_t)f32_to_bf16_rne((a.x * st) * sc.x) |
-                   ((uint32_t)f32_to_bf16_rne((a.y * st) * sc.y) << 16);
-        packed.y = (uint32_t)f32_to_bf16_rne((a.z * st) * sc.z) |
-                   ((uint32_t)f32_to_bf16_rne((a.w * st) * sc.w) << 16);
+        packed.x = f32x2_to_bf16x2_rne((a.x * st) * sc.x,
+                   (a.y * st) * sc.y);
+        packed.y = f32x2_to_bf16x2_rne((a.z * st) * sc.z,
+                   (a.w * st) * sc.w);
         *reinterpret_cast<uint2*>(out + t * ldo + o) = packed;
     }
 }
