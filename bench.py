@@ -448,6 +448,11 @@ def sweep(args):
 
 def main():
     args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "libptpc runs on one GPU (no multi-GPU sharding); "
+                                   "--gpus must be 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
     if args.mfma_ceiling:
         mfma_ceiling(args)
         return
@@ -468,10 +473,6 @@ def main():
             f.write("\n")
         print(json.dumps(rec, indent=1))
         return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
-                          "n_gpus_requested": args.gpus}), flush=True)
-        sys.exit(2)
 
     import numpy as np
     import torch
