@@ -25,7 +25,11 @@
  *     Co % 16 == 0; base pointers 16-byte aligned; bf16 pitches multiples of
  *     8 elements and E4M3 pitches multiples of 16 (16-byte rows).  A zero
  *     extent is a no-op returning PTPC_OK (except as noted for Ci == 0).
- *     The GEMM calls also need Ci, ldq and ldo <= 2^22.
+ *     The weight and GEMM calls also need Ci <= 2^17 (the K range in which
+ *     every partial sum of E4M3 products is exact in double, the accuracy
+ *     reference).  Every call needs row pitches <= 2^22 elements, row
+ *     counts (T, R) and output columns (Co) <= 2^24, and a GEMM at most 2^36
+ *     outputs (T * Co).
  *     Anything else returns PTPC_ERR_UNSUPPORTED / PTPC_ERR_ALIGN.
  *
  * Quantization rule (readings taken where [PTPC] is silent):
@@ -75,7 +79,8 @@ ptpc_status ptpc_quant_act(const void* x, int64_t T, int64_t Ci, int64_t ldx,
 
 /*
  * Size in bytes of the packed weight buffer for a [Ci x Co] weight:
- * Co * roundup(Ci, 128).  Returns 0 for unsupported or empty shapes.
+ * Co * roundup(Ci, 128).  Returns 0 for unsupported or empty shapes
+ * (including Ci > 2^17).
  */
 size_t ptpc_weight_packed_bytes(int64_t Ci, int64_t Co);
 
@@ -213,6 +218,21 @@ ptpc_status ptpc_gemm_tensor(const uint8_t* qx, int64_t ldq, const float* dx,
                              const void* w_packed, const float* dw, int64_t T,
                              int64_t Ci, int64_t Co, void* out, int64_t ldo,
                              void* stream);
+
+/*
+ * ---- Diagnostics ----------------------------------------------------------
+ * Which kernel a call launches for a shape (the choice is made on the host
+ * from the extents alone), as a static string naming the kernel and its
+ * template arguments, e.g. "gemm16_kernel<256,256,2,2>".  NULL for shapes
+ * the call rejects or for which it launches nothing.  Nothing is launched.
+ */
+
+/* Kernel of ptpc_gemm, ptpc_gemm_unfused, ptpc_gemm_unfused_bf16,
+ * ptpc_gemm_tensor and of ptpc_gemm_ws where it does not split K. */
+const char* ptpc_gemm_kernel(int64_t T, int64_t Ci, int64_t Co);
+
+/* Kernel of ptpc_quant_act for T rows of Ci elements. */
+const char* ptpc_quant_act_kernel(int64_t T, int64_t Ci);
 
 #ifdef __cplusplus
 }

@@ -16,9 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libptpc.so")
-PROBE_LIB = os.path.join(PKG, "libmfma_probe.so")
 
-SOURCES = ["ptpc_api.cpp", "quant.hip", "gemm.hip"]
+SOURCES = ["ptpc_api.cpp", "plan.cpp", "quant.hip", "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -40,14 +39,14 @@ def _run(cmd, verbose):
     return r.stdout
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([HIPCC, *FLAGS, *extra_flags, *lang, "-c", os.path.join(CSRC, src),
+        cmds.append([HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src),
                      "-o", obj])
         objs.append(obj)
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
@@ -57,12 +56,6 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
-    # The register-only MFMA throughput probe behind `bench.py --mfma-ceiling`:
-    # its own shared object, not part of the library.
-    ptmp = PROBE_LIB + ".tmp"
-    _run([HIPCC, *FLAGS, *extra_flags, "-x", "hip", "-shared", "-o", ptmp,
-          os.path.join(PKG, "probe", "mfma_peak.hip")], verbose)
-    os.replace(ptmp, PROBE_LIB)
     return LIB
 
 

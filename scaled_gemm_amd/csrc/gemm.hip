@@ -96,7 +96,6 @@ constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 // the MALL, and the 32 tiles an XCD holds at once (4 row x 8 column blocks)
 // share 12 operand blocks per K step.
 constexpr int kXcds = 8;
-constexpr int64_t kCus = 256;
 constexpr int kGroupN = 8;
 __device__ __forceinline__ void tile_of(int i, int gm, int gn, int& tm, int& tn) {
     const int n = gm * gn;
@@ -1518,112 +1517,44 @@ static hipError_t launch_tiles16s(const uint8_t* qx, int64_t ldq, const float* d
     return hipGetLastError();
 }
 
-#ifndef TILE_COST_256x128
-#define TILE_COST_256x128 0.69
-#endif
-#ifndef TILE_COST_256x224
-#define TILE_COST_256x224 0.92
-#endif
-#ifndef TILE_COST_128x128
-#define TILE_COST_128x128 0.55
-#endif
-#ifndef TILE_COST_256x160
-#define TILE_COST_256x160 0.83
-#endif
-#ifndef TILE_COST_192x256
-#define TILE_COST_192x256 0.88
-#endif
-// 65..128 tokens where the tile rule below picks 64x64 tiles: those run
-// gemm16s_kernel (K split inside the workgroup), which needs no workspace
-// and is not split further across workgroups.
-static bool split16_tiles(int64_t T, int64_t Co) {
-    if (T <= 64 || T > 128) return false;
-    auto rounds = [](int64_t tiles) { return (tiles + kCus - 1) / kCus; };
-    auto tiles = [&](int64_t bm, int64_t bn) { return ((T + bm - 1) / bm) * ((Co + bn - 1) / bn); };
-    const int64_t r64 = rounds(tiles(64, 64));
-    return r64 <= rounds(tiles(128, 128)) && r64 <= rounds(tiles(64, 128));
-}
-
 static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
-                       const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
-                       int64_t ldo, float* fp32_out, hipStream_t s, int ts) {
-    // Tile choice: 256x256 keeps the most MFMA work per loaded byte; when it
-    // leaves CUs idle or a badly filled last round, 256x224 (4 waves side by
-    // side along the tokens), 192x256, 256x160, 256x128 or 128x128 -- more
-    // tiles, each costing 0.92, 0.88, 0.83, 0.69 or 0.55 of a 256x256 one,
-    // measured on the 8B / 70B layers -- is taken if its rounds cost less
-    // (256x160: the 70B QKV layer at 1024 tokens, 256 tiles for 256 CUs, 6%
-    // faster than 192x256; 128x128: 256..600 tokens of the 8192-column
-    // layers, where 256-row tiles leave CUs idle, 18-29% faster).
-    auto rounds = [](int64_t tiles) { return (tiles + kCus - 1) / kCus; };
-    auto tiles = [&](int64_t bm, int64_t bn) { return ((T + bm - 1) / bm) * ((Co + bn - 1) / bn); };
-    // Cost in 256x256 tile-times of each tiled form: rounds of 256 CUs times
-    // the measured time of one tile relative to a 256x256 one.
-    const double c256 = (double)rounds(tiles(256, 256));
-    const double c128 = TILE_COST_256x128 * (double)rounds(tiles(256, 128));
-    const double c192 = TILE_COST_192x256 * (double)rounds(tiles(192, 256));
-    const double c224 = TILE_COST_256x224 * (double)rounds(tiles(256, 224));
-    // Up to 64 tokens the weight stream decides.  The tiled kernel reads
-    // each weight byte once per row tile and keeps the activation in LDS, but
-    // with few column tiles it leaves CUs idle; the few-token kernel splits K
-    // inside a workgroup instead.  It is taken unless the tiled grid has at
-    // least two workgroups per CU (32x64 tiles) or one (128x128 tiles): the
-    // crossover measured on the 8B / 70B projection shapes.  Its 64-column
-    // form (half the activation re-reads) pays off from 16 tokens on, once
-    // the 32-column grid no longer fits the CUs in one round.
-    hipError_t e;
-    const double c160 = TILE_COST_256x160 * (double)rounds(tiles(256, 160));
-    const double c1616 = TILE_COST_128x128 * (double)rounds(tiles(128, 128));
-    if (T >= 256 && c1616 < c256 && c1616 < c128 && c1616 < c192 && c1616 < c160 &&
-        c1616 < c224)
-        e = launch_tiles16<128, 128, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T >= 256 && c160 < c256 && c160 < c192 && c160 < c128 && c160 < c224)
-        e = launch_tiles16<256, 160, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T >= 256 && c224 < c256 && c224 < c192 && c224 < c128)
-        e = launch_tiles16<256, 224, 4, 1>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T >= 256 && c128 < c256 && c128 <= c192 && Ci >= 16384)
-        // Long K: the same tile count as 128x256 tiles, whose 8 column slabs
-        // per wave spread the fills more evenly (70B down projection at 1024
-        // tokens: 6% faster; at K = 8192 the 256x128 form was 3-5% faster).
-        e = launch_tiles16<128, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T >= 256 && c128 < c256 && c128 <= c192)
-        e = launch_tiles16<256, 128, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T >= 256 && c192 < c256)
-        e = launch_tiles16<192, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T >= 256)
-        e = launch_tiles16<256, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T > 64) {
-        // 65..255 tokens: the fewest rounds of 256 CUs, and among equal
-        // rounds the smaller tile (more CUs streaming the weight): 128x128
-        // tiles leave most CUs idle on the 8192-column layers.  64x64 tiles
-        // of up to 128 tokens (two row tiles) run gemm16s_kernel, the K
-        // steps split between the waves: 19-48% faster than the same tiles
-        // with a barrier per 64-byte step.  Where the rule picks larger
-        // tiles the split kernel's 64x64 tiles would double the operand
-        // traffic into LDS and lose (70B gate_up at 128 tokens: 1.5x slower).
-        const int64_t r128 = rounds(tiles(128, 128)), r64w = rounds(tiles(64, 128));
-        const int64_t r64 = rounds(tiles(64, 64));
-        if (split16_tiles(T, Co))
-            e = launch_tiles16s(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-        else if (r64 <= r128 && r64 <= r64w)
-            e = launch_tiles<64, 64, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-        else if (r64w <= r128)
-            e = launch_tiles<64, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-        else   // 128x128 tiles: the 16x16x128 kernel, 3-5% faster here (70B gate_up)
-            e = launch_tiles16<128, 128, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    } else if (T > 32 && (Co + 127) / 128 >= kCus)
-        e = launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T > 32 && (Co + 31) / 32 > kCus)
-        e = launch_decode<2, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T > 32)
-        e = launch_decode<2, 1, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T > 8 && (Co + 63) / 64 >= 2 * kCus)
-        e = launch_tiles<32, 64, 1, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else if (T > 8 && (Co + 31) / 32 > kCus)
-        e = launch_decode<1, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    else
-        e = launch_decode<1, 1, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
-    return e;
+                              const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
+                              int64_t ldo, float* fp32_out, hipStream_t s, int ts) {
+    switch (gemm_plan(T, Ci, Co)) {
+        case GemmPlan::k16_256x256:
+            return launch_tiles16<256, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k16_192x256:
+            return launch_tiles16<192, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k16_256x224:
+            return launch_tiles16<256, 224, 4, 1>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k16_256x160:
+            return launch_tiles16<256, 160, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k16_128x256:
+            return launch_tiles16<128, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k16_256x128:
+            return launch_tiles16<256, 128, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k16_128x128:
+            return launch_tiles16<128, 128, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k16s_64x64:
+            return launch_tiles16s(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k32_64x64:
+            return launch_tiles<64, 64, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k32_64x128:
+            return launch_tiles<64, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k32_128x128:
+            return launch_tiles<128, 128, 2, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k32_32x64:
+            return launch_tiles<32, 64, 1, 2, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::kDecode_2x2:
+            return launch_decode<2, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::kDecode_2x1:
+            return launch_decode<2, 1, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::kDecode_1x2:
+            return launch_decode<1, 2, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::kDecode_1x1:
+            return launch_decode<1, 1, 4, 4>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+    }
+    return hipErrorInvalidValue;
 }
 
 static int64_t rescale_blocks(int64_t T, int64_t Co) {
@@ -1641,19 +1572,6 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
     hipLaunchKernelGGL(rescale_kernel, dim3((unsigned)rescale_blocks(T, Co)), dim3(256), 0, s,
                        fp32_out, dx, dw, T, Co, out, ldo);
     return hipGetLastError();
-}
-
-// Split-K plan for shapes whose tiled grid leaves most CUs idle: 65..255
-// tokens on 128x128 tiles, K cut into S ranges of at least 16 steps so that
-// tiles x S fills the CUs.  Returns S (1: no split).
-int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co) {
-    if (T <= 64 || T >= 256 || split16_tiles(T, Co)) return 1;
-    const int64_t tiles = ((T + 127) / 128) * ((Co + 127) / 128);
-    int64_t S = kCus / tiles;
-    const int64_t nks = round_up_k(Ci) / BK;
-    if (S > nks / 16) S = nks / 16;
-    if (S > 8) S = 8;
-    return S < 2 ? 1 : (int)S;
 }
 
 hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,

@@ -8,6 +8,10 @@
 
 namespace ptpc {
 
+// Compute units of the target GPU (MI355X): the tile rules count rounds of
+// this many workgroups.
+constexpr int64_t kCus = 256;
+
 // K extent of the packed weight: whole 128-byte K tiles.
 inline int64_t round_up_k(int64_t Ci) { return (Ci + 127) / 128 * 128; }
 
@@ -28,6 +32,26 @@ hipError_t launch_quant_weight_static(const uint16_t* w, int64_t Ci, int64_t Co,
 
 hipError_t launch_unpack_weight(const uint8_t* packed, int64_t Ci, int64_t Co, uint8_t* qw,
                                 hipStream_t s);
+
+// The GEMM kernel and tile ptpc_gemm (and both two-step forms) launch for a
+// shape, chosen on the host from T, Ci and Co alone.
+enum class GemmPlan : int {
+    k16_256x256, k16_192x256, k16_256x224, k16_256x160, k16_128x256, k16_256x128, k16_128x128,
+    k16s_64x64, k32_64x64, k32_64x128, k32_128x128, k32_32x64,
+    kDecode_2x2, kDecode_2x1, kDecode_1x2, kDecode_1x1,
+};
+GemmPlan gemm_plan(int64_t T, int64_t Ci, int64_t Co);
+const char* gemm_plan_name(GemmPlan p);
+
+// Launch shape of the activation quantizer for rows of Ci elements: G
+// threads per row holding VPT 16-byte vectors each, or G = 0 for the two-pass
+// long-row kernel; and its kernel's name (for a row count and length).
+struct ActPlan {
+    int G;
+    int vpt;
+};
+ActPlan act_plan(int64_t Ci);
+const char* quant_act_plan_name(int64_t T, int64_t Ci);
 
 // fp32_out == nullptr: fused epilogue writing bf16 `out`.
 // fp32_out != nullptr: the GEMM stores unscaled fp32 sums there ([T x Co],

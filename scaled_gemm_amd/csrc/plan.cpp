@@ -1,0 +1,168 @@
+// Kernel choice of libptpc, made on the host from the extents alone: which
+// GEMM kernel and tile, the split-K plan of ptpc_gemm_ws, and the launch shape
+// of the activation quantizer.  Plain host C++ (no device code), shared by
+// the launchers and the diagnostic queries of the C ABI.
+#include "kernels.h"
+
+namespace ptpc {
+
+// Measured time of one tile relative to a 256x256 tile at the same K, on
+// the 8B / 70B layers (256x224, 192x256 and 256x128 on the 32x32x64 kernel,
+// 256x160 and 128x128 on the 16x16x128 one).
+constexpr double kCost256x128 = 0.69;
+constexpr double kCost256x224 = 0.92;
+constexpr double kCost128x128 = 0.55;
+constexpr double kCost256x160 = 0.83;
+constexpr double kCost192x256 = 0.88;
+
+// 65..128 tokens where the tile rule below picks 64x64 tiles: those run
+// gemm16s_kernel (K split inside the workgroup), which needs no workspace
+// and is not split further across workgroups.
+static bool split16_tiles(int64_t T, int64_t Co) {
+    if (T <= 64 || T > 128) return false;
+    auto rounds = [](int64_t tiles) { return (tiles + kCus - 1) / kCus; };
+    auto tiles = [&](int64_t bm, int64_t bn) { return ((T + bm - 1) / bm) * ((Co + bn - 1) / bn); };
+    const int64_t r64 = rounds(tiles(64, 64));
+    return r64 <= rounds(tiles(128, 128)) && r64 <= rounds(tiles(64, 128));
+}
+
+GemmPlan gemm_plan(int64_t T, int64_t Ci, int64_t Co) {
+    auto rounds = [](int64_t tiles) { return (tiles + kCus - 1) / kCus; };
+    auto tiles = [&](int64_t bm, int64_t bn) { return ((T + bm - 1) / bm) * ((Co + bn - 1) / bn); };
+    if (T >= 256) {
+        // 256x256 keeps the most MFMA work per loaded byte; when it leaves
+        // CUs idle or a badly filled last round, 256x224 (4 waves side by
+        // side along the tokens), 192x256, 256x160, 256x128 or 128x128 -- more
+        // tiles, each cheaper -- is taken if its rounds of 256 CUs cost less
+        // (256x160: the 70B QKV layer at 1024 tokens, 256 tiles for 256 CUs,
+        // 6% faster than 192x256; 128x128: 256..600 tokens of the 8192-column
+        // layers, where 256-row tiles leave CUs idle, 18-29% faster).  Costs
+        // are in 256x256 tile-times: rounds times the relative tile cost.
+        const double c256 = (double)rounds(tiles(256, 256));
+        const double c128 = kCost256x128 * (double)rounds(tiles(256, 128));
+        const double c192 = kCost192x256 * (double)rounds(tiles(192, 256));
+        const double c224 = kCost256x224 * (double)rounds(tiles(256, 224));
+        const double c160 = kCost256x160 * (double)rounds(tiles(256, 160));
+        const double c1616 = kCost128x128 * (double)rounds(tiles(128, 128));
+        if (c1616 < c256 && c1616 < c128 && c1616 < c192 && c1616 < c160 && c1616 < c224)
+            return GemmPlan::k16_128x128;
+        if (c160 < c256 && c160 < c192 && c160 < c128 && c160 < c224) return GemmPlan::k16_256x160;
+        if (c224 < c256 && c224 < c192 && c224 < c128) return GemmPlan::k16_256x224;
+        // Long K: the same tile count as 256x128 tiles, whose eight column
+        // slabs per wave spread the fills more evenly (70B down projection at
+        // 1024 tokens: 6% faster; at K = 8192 the 256x128 form was 3-5% faster).
+        if (c128 < c256 && c128 <= c192 && Ci >= 16384) return GemmPlan::k16_128x256;
+        if (c128 < c256 && c128 <= c192) return GemmPlan::k16_256x128;
+        if (c192 < c256) return GemmPlan::k16_192x256;
+        return GemmPlan::k16_256x256;
+    }
+    if (T > 64) {
+        // 65..255 tokens: the fewest rounds of 256 CUs, and among equal
+        // rounds the smaller tile (more CUs streaming the weight): 128x128
+        // tiles leave most CUs idle on the 8192-column layers.  64x64 tiles
+        // of up to 128 tokens (two row tiles) run gemm16s_kernel, the K
+        // steps split between the waves: 19-48% faster than the same tiles
+        // with a barrier per 64-byte step.  Where the rule picks larger
+        // tiles the split kernel's 64x64 tiles would double the operand
+        // traffic into LDS and lose (70B gate_up at 128 tokens: 1.5x slower).
+        const int64_t r128 = rounds(tiles(128, 128)), r64w = rounds(tiles(64, 128));
+        const int64_t r64 = rounds(tiles(64, 64));
+        if (split16_tiles(T, Co)) return GemmPlan::k16s_64x64;
+        if (r64 <= r128 && r64 <= r64w) return GemmPlan::k32_64x64;
+        if (r64w <= r128) return GemmPlan::k32_64x128;
+        return GemmPlan::k16_128x128;   // the 16x16x128 kernel, 3-5% faster here (70B gate_up)
+    }
+    // Up to 64 tokens the weight stream decides.  The tiled kernel reads
+    // each weight byte once per row tile and keeps the activation in LDS, but
+    // with few column tiles it leaves CUs idle; the few-token kernel splits K
+    // inside a workgroup instead.  It is taken unless the tiled grid has at
+    // least two workgroups per CU (32x64 tiles) or one (128x128 tiles): the
+    // crossover measured on the 8B / 70B projection shapes.  Its 64-column
+    // form (half the activation re-reads) pays off from 16 tokens on, once
+    // the 32-column grid no longer fits the CUs in one round.
+    if (T > 32 && (Co + 127) / 128 >= kCus) return GemmPlan::k32_128x128;
+    if (T > 32 && (Co + 31) / 32 > kCus) return GemmPlan::kDecode_2x2;
+    if (T > 32) return GemmPlan::kDecode_2x1;
+    if (T > 8 && (Co + 63) / 64 >= 2 * kCus) return GemmPlan::k32_32x64;
+    if (T > 8 && (Co + 31) / 32 > kCus) return GemmPlan::kDecode_1x2;
+    return GemmPlan::kDecode_1x1;
+}
+
+const char* gemm_plan_name(GemmPlan p) {
+    switch (p) {
+        case GemmPlan::k16_256x256: return "gemm16_kernel<256,256,2,2>";
+        case GemmPlan::k16_192x256: return "gemm16_kernel<192,256,2,2>";
+        case GemmPlan::k16_256x224: return "gemm16_kernel<256,224,4,1>";
+        case GemmPlan::k16_256x160: return "gemm16_kernel<256,160,2,2>";
+        case GemmPlan::k16_128x256: return "gemm16_kernel<128,256,2,2>";
+        case GemmPlan::k16_256x128: return "gemm16_kernel<256,128,2,2>";
+        case GemmPlan::k16_128x128: return "gemm16_kernel<128,128,2,2>";
+        case GemmPlan::k16s_64x64: return "gemm16s_kernel";
+        case GemmPlan::k32_64x64: return "gemm_kernel<64,64,2,2,4>";
+        case GemmPlan::k32_64x128: return "gemm_kernel<64,128,2,2,4>";
+        case GemmPlan::k32_128x128: return "gemm_kernel<128,128,2,2,4>";
+        case GemmPlan::k32_32x64: return "gemm_kernel<32,64,1,2,4>";
+        case GemmPlan::kDecode_2x2: return "gemm_decode_kernel<2,2,4,4>";
+        case GemmPlan::kDecode_2x1: return "gemm_decode_kernel<2,1,4,4>";
+        case GemmPlan::kDecode_1x2: return "gemm_decode_kernel<1,2,4,4>";
+        case GemmPlan::kDecode_1x1: return "gemm_decode_kernel<1,1,4,4>";
+    }
+    return nullptr;
+}
+
+// Split-K plan for shapes whose tiled grid leaves most CUs idle: 65..255
+// tokens on 128x128 tiles, K cut into S ranges of at least 16 steps so that
+// tiles x S fills the CUs.  Returns S (1: no split).
+int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co) {
+    if (T <= 64 || T >= 256 || split16_tiles(T, Co)) return 1;
+    const int64_t tiles = ((T + 127) / 128) * ((Co + 127) / 128);
+    int64_t S = kCus / tiles;
+    const int64_t nks = round_up_k(Ci) / 64;   // 64-byte K steps of the split kernel
+    if (S > nks / 16) S = nks / 16;
+    if (S > 8) S = 8;
+    return S < 2 ? 1 : (int)S;
+}
+
+static int pow2_ceil(int64_t v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+// Launch shape of the activation quantizer for rows of Ci elements: G
+// threads per row holding VPT 16-byte vectors each, or (G = 0) the two-pass
+// kernel for rows longer than 256 threads x 16 vectors.  Rows of 256 or more
+// vectors get a whole 256-thread workgroup (more loads in flight per row
+// beat more vectors per thread); shorter rows share a workgroup, about 8
+// vectors per thread, at least 16 threads.  Reachable shapes: G = 16 with
+// VPT 1..8 (up to 128 vectors), G = 32 with VPT 8 (129..255 vectors), G = 256
+// with VPT 1..16, and the long-row kernel.
+ActPlan act_plan(int64_t Ci) {
+    const int64_t nchunk = Ci / 8;
+    int64_t G = 256;
+    if (nchunk < 256) {
+        G = pow2_ceil((nchunk + 7) / 8);
+        if (G < 16) G = 16;
+    }
+    const int64_t per = (nchunk + G - 1) / G;
+    if (per > 16) return {0, 0};
+    return {(int)G, pow2_ceil(per)};
+}
+
+const char* quant_act_plan_name(int64_t T, int64_t Ci) {
+    if (T <= 0) return nullptr;
+    if (Ci == 0) return "fill_f32_kernel";
+    const ActPlan p = act_plan(Ci);
+    static const char* const names[] = {
+        "quant_act_kernel<16,1>",   "quant_act_kernel<16,2>",  "quant_act_kernel<16,4>",
+        "quant_act_kernel<16,8>",   "quant_act_kernel<32,8>",  "quant_act_kernel<256,1>",
+        "quant_act_kernel<256,2>",  "quant_act_kernel<256,4>", "quant_act_kernel<256,8>",
+        "quant_act_kernel<256,16>"};
+    if (p.G == 0) return "quant_act_long_kernel";
+    const int lv = __builtin_ctz((unsigned)p.vpt);
+    if (p.G == 16) return names[lv];
+    if (p.G == 32) return names[4];
+    return names[5 + lv];
+}
+
+}  // namespace ptpc

@@ -132,24 +132,6 @@ static hipError_t launch_act(const uint16_t* x, int64_t T, int64_t Ci, int64_t l
     return hipGetLastError();
 }
 
-template <int G>
-static hipError_t launch_act_g(int vpt, const uint16_t* x, int64_t T, int64_t Ci, int64_t ldx,
-                               uint8_t* qx, int64_t ldq, float* dx, hipStream_t s) {
-    switch (vpt) {
-        case 1: return launch_act<G, 1>(x, T, Ci, ldx, qx, ldq, dx, s);
-        case 2: return launch_act<G, 2>(x, T, Ci, ldx, qx, ldq, dx, s);
-        case 4: return launch_act<G, 4>(x, T, Ci, ldx, qx, ldq, dx, s);
-        case 8: return launch_act<G, 8>(x, T, Ci, ldx, qx, ldq, dx, s);
-        default: return launch_act<G, 16>(x, T, Ci, ldx, qx, ldq, dx, s);
-    }
-}
-
-static int pow2_ceil(int64_t v) {
-    int p = 1;
-    while (p < v) p <<= 1;
-    return p;
-}
-
 hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t Ci, int64_t ldx,
                             uint8_t* qx, int64_t ldq, float* dx, hipStream_t s) {
     if (Ci == 0) {
@@ -157,28 +139,27 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t Ci, int64_t ld
                            dx, T, 1.0f);
         return hipGetLastError();
     }
-    const int64_t nchunk = Ci / 8;
-    // Rows of 256 or more 16-byte vectors get a whole 256-thread workgroup
-    // (more loads in flight per row beat more vectors per thread); shorter
-    // rows share a workgroup, about 8 vectors per thread, at least 16 threads.
-    int64_t G = 256;
-    if (nchunk < 256) {
-        G = pow2_ceil((nchunk + 7) / 8);
-        if (G < 16) G = 16;
-    }
-    const int64_t per = (nchunk + G - 1) / G;
-    if (per > 16) {
+    const ActPlan p = act_plan(Ci);
+    if (p.G == 0) {
         hipLaunchKernelGGL(quant_act_long_kernel, dim3((unsigned)T), dim3(256), 0, s,
                            x, Ci, ldx, qx, ldq, dx);
         return hipGetLastError();
     }
-    const int vpt = pow2_ceil(per);
-    switch (G) {
-        case 16: return launch_act_g<16>(vpt, x, T, Ci, ldx, qx, ldq, dx, s);
-        case 32: return launch_act_g<32>(vpt, x, T, Ci, ldx, qx, ldq, dx, s);
-        case 64: return launch_act_g<64>(vpt, x, T, Ci, ldx, qx, ldq, dx, s);
-        case 128: return launch_act_g<128>(vpt, x, T, Ci, ldx, qx, ldq, dx, s);
-        default: return launch_act_g<256>(vpt, x, T, Ci, ldx, qx, ldq, dx, s);
+    if (p.G == 16) {
+        switch (p.vpt) {
+            case 1: return launch_act<16, 1>(x, T, Ci, ldx, qx, ldq, dx, s);
+            case 2: return launch_act<16, 2>(x, T, Ci, ldx, qx, ldq, dx, s);
+            case 4: return launch_act<16, 4>(x, T, Ci, ldx, qx, ldq, dx, s);
+            default: return launch_act<16, 8>(x, T, Ci, ldx, qx, ldq, dx, s);
+        }
+    }
+    if (p.G == 32) return launch_act<32, 8>(x, T, Ci, ldx, qx, ldq, dx, s);
+    switch (p.vpt) {
+        case 1: return launch_act<256, 1>(x, T, Ci, ldx, qx, ldq, dx, s);
+        case 2: return launch_act<256, 2>(x, T, Ci, ldx, qx, ldq, dx, s);
+        case 4: return launch_act<256, 4>(x, T, Ci, ldx, qx, ldq, dx, s);
+        case 8: return launch_act<256, 8>(x, T, Ci, ldx, qx, ldq, dx, s);
+        default: return launch_act<256, 16>(x, T, Ci, ldx, qx, ldq, dx, s);
     }
 }
 

@@ -23,6 +23,17 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def nan_filled(T, Co):
+    """A bf16 [T, Co] output buffer on the GPU holding NaN in every element."""
+    return torch.full((T, Co), float("nan"), dtype=torch.bfloat16, device="cuda")
+
+
+def no_nan(t: torch.Tensor, what: str):
+    """Every element of a GPU output was written (none is still NaN)."""
+    n = int(torch.isnan(t).sum().item())
+    assert n == 0, f"{what}: {n} outputs never written (still NaN)"
+
+
 def check_close(gpu_bits: np.ndarray, ref: np.ndarray, what: str):
     """The acceptance bar on a set of outputs (full or sampled)."""
     got = bf16_bits_to_f64(gpu_bits)

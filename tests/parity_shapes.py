@@ -1,0 +1,110 @@
+"""The shapes the GPU parity tests run, in one place (host side only).
+
+The GPU tests take their cases from here, and ``test_kernel_coverage.py``
+checks on the CPU, through the library's kernel-choice queries, that these
+cases together launch every GEMM and activation-quantization kernel the
+library can pick.
+"""
+import workloads
+
+# Whole outputs against the full oracle: (name, T, Ci, Co).
+FULL_CASES = [
+    ("tiny", 16, 256, 512),
+    ("8b_qkv_decode", 32, 4096, 6144),
+    ("ragged", 300, 1040, 784),
+    ("ragged", 257, 384, 272),
+    ("ragged", 1, 16, 16),
+    ("ragged", 3, 144, 48),
+    ("ragged", 33, 272, 2064),
+    ("ragged", 97, 400, 1040),
+    ("ragged", 130, 272, 8208),      # 64x128 tiles (65..255 tokens, fewest rounds)
+    ("ragged", 200, 144, 1040),      # 64x64 tiles, four row tiles
+    ("ragged", 48, 272, 10256),
+    ("ragged", 48, 272, 32784),      # 128x128 tiles of the 32x32x64 kernel at 33..64 tokens
+    ("ragged", 20, 144, 32784),
+    ("ragged", 24, 208, 8208),
+    ("ragged", 600, 256, 2048),
+    ("ragged", 513, 512, 2064),
+    ("ragged", 600, 144, 22000),
+    ("ragged", 500, 144, 28656),
+    # 128-byte K steps run in periods of 6, the rest one by one: 12, 7 and 11
+    # steps (remainders 0, 1 and 5; the cases above cover 2, 3 and 4)
+    ("ragged", 280, 1536, 528),
+    ("ragged", 272, 880, 1296),
+    ("ragged", 520, 1392, 400),
+    # 65..128 tokens on 64x64 tiles: K steps dealt to 4 waves (1 step: three
+    # waves idle; 13 and 27 steps: uneven counts per wave)
+    ("ragged", 100, 16, 2064),
+    ("ragged", 65, 1552, 528),
+    ("ragged", 120, 3344, 1040),
+    ("ragged", 200, 272, 36864),     # 128x128 tiles of the 16x16x128 kernel at 65..255 tokens
+    # near the longest K the contract accepts (2^17), with a K tail past the
+    # last whole 128-byte step (the few-token kernel)
+    ("ragged", 8, 131072 - 16, 256),
+]
+
+FULL_SEEDS = [("tiny", 1), ("tiny", 2), ("8b_qkv_decode", 1), ("8b_qkv_decode", 2)]
+
+# Sampled outputs at full size; these select each of the other tile shapes of
+# the 128-byte-step kernel, with K remainders the full-size configs do not
+# have (ragged K, periods of 6 steps plus 1, 5, 0, 1).  (T, Ci, Co).
+TILE_CASES = [
+    (4096, 1648, 4096),     # 256x256 tiles, 13 K steps
+    (1536, 592, 8192),      # 192x256 tiles, 5 K steps
+    (1024, 880, 10240),     # 256x160 tiles, 7 K steps
+    (1024, 752, 14336),     # 256x224 tiles, 6 K steps
+    (512, 16400, 1024),     # 128x256 tiles (long K), 129 K steps
+    (512, 1040, 4096),      # 128x128 tiles at 256+ tokens, 9 K steps
+    (256, 131072 - 16, 512),  # K near the contract's 2^17 limit, 128x128 tiles, 1024 K steps
+]
+
+CONFIG_CASES = ["8b_gate_up", "70b_down"]
+
+# 70B layer shapes at token counts outside the sweep (sampled outputs):
+# (layer, T).  64 tokens of the gate_up layer run 128x128 tiles of the
+# 32x32x64 kernel (every CU gets one).
+EXTRA_SWEEP_CASES = [("gate_up", 64)]
+
+PER_TENSOR_CASES = [("tiny", 16, 256, 512), ("ragged", 48, 272, 10256),
+                    ("ragged", 300, 1040, 784), ("ragged", 1, 16, 16),
+                    ("8b_qkv_decode", 32, 4096, 6144),
+                    ("ragged", 100, 528, 1040)]   # the K-split 64x64 tiles, scalar scales
+
+# Epilogue edge values: T picks the kernel family (Ci = 4112, Co = 528).
+EPILOGUE_T = [16, 100, 200, 512]
+EPILOGUE_CI, EPILOGUE_CO = 4112, 528
+
+PITCHED_T = [70, 300]                # Ci = 528, Co = 208
+PITCHED_CI, PITCHED_CO = 528, 208
+
+# Activation rows longer than one workgroup holds in registers (the two-pass
+# kernel): (T, Ci).
+LONG_ROW_CASES = [(7, 40960)]
+
+# Row lengths of the exhaustive (x, amax) quantizer check.
+EXHAUSTIVE_CI = [512, 1024, 2048, 4096, 8192, 16384, 24576, 28672, 32768]
+
+
+def gemm_shapes():
+    """Every (T, Ci, Co) a GPU test sends through ptpc_gemm."""
+    out = [(T, Ci, Co) for _, T, Ci, Co in FULL_CASES]
+    out += [(workloads.CONFIGS[n].T, workloads.CONFIGS[n].Ci, workloads.CONFIGS[n].Co)
+            for n, _ in FULL_SEEDS]
+    out += list(TILE_CASES)
+    out += [(workloads.CONFIGS[n].T, workloads.CONFIGS[n].Ci, workloads.CONFIGS[n].Co)
+            for n in CONFIG_CASES]
+    for layer, (Ci, Co) in workloads.SWEEP_LAYERS.items():
+        out += [(T, Ci, Co) for T in workloads.SWEEP_T]
+    out += [(T, *workloads.SWEEP_LAYERS[layer]) for layer, T in EXTRA_SWEEP_CASES]
+    out += [(T, Ci, Co) for _, T, Ci, Co in PER_TENSOR_CASES]
+    out += [(T, EPILOGUE_CI, EPILOGUE_CO) for T in EPILOGUE_T]
+    out += [(T, PITCHED_CI, PITCHED_CO) for T in PITCHED_T]
+    return out
+
+
+def quant_act_shapes():
+    """Every (T, Ci) a GPU test sends through ptpc_quant_act."""
+    out = [(T, Ci) for T, Ci, _ in gemm_shapes()]
+    out += list(LONG_ROW_CASES)
+    out += [(2, Ci) for Ci in EXHAUSTIVE_CI]
+    return out

@@ -94,6 +94,14 @@ def test_quant_weight_validation(L):
     assert f(A, 256, 512, 512, MIS, C, None) == 4
     assert L.ptpc_unpack_weight(NULL, 256, 512, B, None) == 1
     assert L.ptpc_unpack_weight(A, 256, 500, B, None) == 3
+    # K beyond 2^17 (the GEMM's limit) is refused before anything is
+    # launched, by every weight call and the size query
+    big = (1 << 17) + 16
+    assert f(A, big, 512, 512, B, C, None) == 3
+    assert L.ptpc_quant_weight_static(A, big, 512, 512, B, C, None) == 3
+    assert L.ptpc_unpack_weight(A, big, 512, B, None) == 3
+    assert L.ptpc_weight_packed_bytes(big, 512) == 0
+    assert L.ptpc_weight_packed_bytes(1 << 17, 512) == 512 << 17
 
 
 def test_gemm_validation(L):
@@ -113,8 +121,9 @@ def test_gemm_validation(L):
         assert f(A, 256, B, C, D, 4, 256, 512, NULL, 512) == 1
         assert f(MIS, 256, B, C, D, 4, 256, 512, E, 512) == 4
         assert f(A, 256, B, C, D, 4, 256, 512, E, 516) == 4
-        assert f(A, (1 << 22) + 16, B, C, D, 4, 256, 512, E, 512) == 3
-        assert f(A, (1 << 22) + 16, B, C, D, 4, (1 << 22) + 16, 512, E, 512) == 3
+        assert f(A, (1 << 22) + 16, B, C, D, 4, 256, 512, E, 512) == 3      # ldq > 2^22
+        assert f(A, (1 << 17) + 16, B, C, D, 4, (1 << 17) + 16, 512, E, 512) == 3   # Ci > 2^17
+        assert f(A, 256, B, C, D, 4, 256, 512, E, (1 << 22) + 16) == 3      # ldo > 2^22
     assert L.ptpc_gemm_unfused(A, 256, B, C, D, 4, 256, 512, E, 512, NULL, None) == 1
     assert L.ptpc_gemm_unfused_bf16(A, 256, B, C, D, 4, 256, 512, E, 512, NULL, None) == 1
     assert L.ptpc_gemm_unfused_bf16(A, 256, B, C, D, 4, 256, 512, E, 512, MIS, None) == 4

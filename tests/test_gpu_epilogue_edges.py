@@ -21,6 +21,7 @@ import pytest
 import torch
 
 import oracle
+import parity_shapes as ps
 import workloads
 from gpu_helpers import bits_to_dev, dev_to_bits
 
@@ -156,9 +157,9 @@ def same_bits(got, want, what):
 # tiles, 200 the 128x128 / 64x128 tiles (and 4 K ranges through the workspace
 # form), 512 the 16x16x128 tile kernel.
 @pytest.mark.gpu
-@pytest.mark.parametrize("T", [16, 100, 200, 512])
+@pytest.mark.parametrize("T", ps.EPILOGUE_T)
 def test_epilogue_edge_values(gpu_lib, T):
-    Ci, Co = 4112, 528
+    Ci, Co = ps.EPILOGUE_CI, ps.EPILOGUE_CO
     note(f"epilogue edges T={T} Ci={Ci} Co={Co}")
     x, w, dx, dw = edge_case(T, Ci, Co, seed=T)
     qx_o, qw_o, want, ws_want, want_bf = expected(x, w, dx, dw)

@@ -14,9 +14,10 @@ import pytest
 import torch
 
 import oracle
+import parity_shapes as ps
 import workloads
-from gpu_helpers import (bits_to_dev, check_close, dev_to_bits, oracle_sampled_ref,
-                         packed_byte_index, sample_indices)
+from gpu_helpers import (bits_to_dev, check_close, dev_to_bits, nan_filled, no_nan,
+                         oracle_sampled_ref, packed_byte_index, sample_indices)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,14 +44,19 @@ def run_path(x_bits, w_bits):
     """Quantize X and W and run both GEMMs on the GPU; return host copies."""
     x = bits_to_dev(x_bits)
     w = bits_to_dev(w_bits)
+    T, Co = x_bits.shape[0], w_bits.shape[1]
     qx, dx = sg.quant_act(x)
     pw = sg.quant_weight(w)
-    out = sg.gemm(qx, dx, pw)
-    out2 = sg.gemm_unfused(qx, dx, pw)
-    ws3 = torch.empty_like(out)
-    out3 = sg.gemm_unfused_bf16(qx, dx, pw, workspace=ws3)
+    # every output starts as NaN: a tile the kernels skip cannot pass
+    out = sg.gemm(qx, dx, pw, out=nan_filled(T, Co))
+    out2 = sg.gemm_unfused(qx, dx, pw, out=nan_filled(T, Co))
+    ws3 = nan_filled(T, Co)
+    out3 = sg.gemm_unfused_bf16(qx, dx, pw, out=nan_filled(T, Co), workspace=ws3)
     qw = sg.unpack_weight(pw)
     torch.cuda.synchronize()
+    for o, what in ((out, "fused"), (out2, "two-step"), (out3, "bf16 two-step"),
+                    (ws3, "bf16 intermediate")):
+        no_nan(o, what)
     return dict(qx=qx.cpu().numpy(), dx=dx.cpu().numpy(), qw=qw.cpu().numpy(),
                 dw=pw.dw.cpu().numpy(), out=dev_to_bits(out), out2=dev_to_bits(out2),
                 out3=dev_to_bits(out3), ws3=dev_to_bits(ws3), packed=pw.data.cpu().numpy())
@@ -96,40 +102,7 @@ def check_quant(g, x_bits, w_bits, what):
 # ---------------------------------------------------------------------------
 # small and ragged shapes: whole outputs against the full oracle
 # ---------------------------------------------------------------------------
-FULL_CASES = [
-    ("tiny", 16, 256, 512),
-    ("8b_qkv_decode", 32, 4096, 6144),
-    ("ragged", 300, 1040, 784),
-    ("ragged", 257, 384, 272),
-    ("ragged", 1, 16, 16),
-    ("ragged", 3, 144, 48),
-    ("ragged", 33, 272, 2064),
-    ("ragged", 97, 400, 1040),
-    ("ragged", 130, 272, 8208),      # 64x128 tiles (65..255 tokens, fewest rounds)
-    ("ragged", 200, 144, 1040),      # 64x64 tiles, four row tiles
-    ("ragged", 48, 272, 10256),
-    ("ragged", 20, 144, 32784),
-    ("ragged", 24, 208, 8208),
-    ("ragged", 600, 256, 2048),
-    ("ragged", 513, 512, 2064),
-    ("ragged", 600, 144, 22000),
-    ("ragged", 500, 144, 28656),
-    # 128-byte K steps run in periods of 6, the rest one by one: 12, 7 and 11
-    # steps (remainders 0, 1 and 5; the cases above cover 2, 3 and 4)
-    ("ragged", 280, 1536, 528),
-    ("ragged", 272, 880, 1296),
-    ("ragged", 520, 1392, 400),
-    # 65..128 tokens on 64x64 tiles: K steps dealt to 4 waves (1 step: three
-    # waves idle; 13 and 27 steps: uneven counts per wave)
-    ("ragged", 100, 16, 2064),
-    ("ragged", 65, 1552, 528),
-    ("ragged", 120, 3344, 1040),
-    ("ragged", 200, 272, 36864),     # 128x128 tiles of the 16x16x128 kernel at 65..255 tokens
-]
-
-
-@pytest.mark.parametrize("name,seed", [("tiny", 1), ("tiny", 2), ("8b_qkv_decode", 1),
-                                       ("8b_qkv_decode", 2)])
+@pytest.mark.parametrize("name,seed", ps.FULL_SEEDS)
 def test_full_parity_other_seeds(name, seed):
     note(f"full parity {name} seed={seed}")
     _, x, w = workloads.make(name, seed=seed)
@@ -156,7 +129,7 @@ def ragged_inputs(T, Ci, Co):
     return x, w
 
 
-@pytest.mark.parametrize("name,T,Ci,Co", FULL_CASES)
+@pytest.mark.parametrize("name,T,Ci,Co", ps.FULL_CASES)
 def test_full_parity(name, T, Ci, Co):
     note(f"full parity {name} T={T} Ci={Ci} Co={Co}")
     if name == "ragged":
@@ -187,31 +160,25 @@ def sampled_case(x, w, what, seed):
     return g
 
 
-# The small cases above all get 256x128 tiles; these shapes select each of
-# the other tile shapes of the 128-byte-step kernel, with K remainders the
-# full-size configs do not have (ragged K, periods of 6 steps plus 1, 5, 0, 1).
-TILE_CASES = [
-    (4096, 1648, 4096),     # 256x256 tiles, 13 K steps
-    (1536, 592, 8192),      # 192x256 tiles, 5 K steps
-    (1024, 880, 10240),     # 256x160 tiles, 7 K steps
-    (1024, 752, 14336),     # 256x224 tiles, 6 K steps
-    (512, 16400, 1024),     # 128x256 tiles (long K), 129 K steps
-    (512, 1040, 4096),      # 128x128 tiles at 256+ tokens, 9 K steps
-]
-
-
-@pytest.mark.parametrize("T,Ci,Co", TILE_CASES)
+@pytest.mark.parametrize("T,Ci,Co", ps.TILE_CASES)
 def test_tile_shape_parity(T, Ci, Co):
     note(f"tile-shape parity T={T} Ci={Ci} Co={Co}")
     x, w = ragged_inputs(T, Ci, Co)
     sampled_case(x, w, f"T={T} Ci={Ci} Co={Co}", seed=T + Ci)
 
 
-@pytest.mark.parametrize("name", ["8b_gate_up", "70b_down"])
+@pytest.mark.parametrize("name", ps.CONFIG_CASES)
 def test_config_parity(name):
     note(f"config parity {name}")
     shape, x, w = workloads.make(name)
     sampled_case(x, w, name, seed=1)
+
+
+@pytest.mark.parametrize("layer,T", ps.EXTRA_SWEEP_CASES)
+def test_extra_sweep_shape_parity(layer, T):
+    note(f"70b {layer} T={T} (sampled)")
+    shape, x, w = workloads.make("70b_sweep", T=T, layer=layer)
+    sampled_case(x, w, shape.name, seed=T)
 
 
 @pytest.mark.parametrize("layer", list(workloads.SWEEP_LAYERS))
@@ -232,8 +199,13 @@ def test_sweep_parity(layer):
         note(f"70b sweep {layer} T={T}")
         xd = bits_to_dev(x)
         qx, dx = sg.quant_act(xd)
-        out = dev_to_bits(sg.gemm(qx, dx, pw)).reshape(T, -1)
-        out2 = dev_to_bits(sg.gemm_unfused(qx, dx, pw)).reshape(T, -1)
+        o1 = sg.gemm(qx, dx, pw, out=nan_filled(T, shape.Co))
+        o2 = sg.gemm_unfused(qx, dx, pw, out=nan_filled(T, shape.Co))
+        no_nan(o1, f"{shape.name} fused")
+        no_nan(o2, f"{shape.name} two-step")
+        out = dev_to_bits(o1).reshape(T, -1)
+        out2 = dev_to_bits(o2).reshape(T, -1)
+        del o1, o2
         qx_o, dx_o = oracle.quant_act(x)
         assert np.array_equal(dx.cpu().numpy(), dx_o)
         assert np.array_equal(qx.cpu().numpy(), qx_o)
@@ -254,7 +226,7 @@ def test_quant_act_exhaustive_pairs():
     input the quantizer can see (rows of various lengths exercise each
     launch shape)."""
     amax_all = np.arange(1, 0x7F80, dtype=np.int32)       # positive finite bf16
-    buckets = [512, 1024, 2048, 4096, 8192, 16384, 24576, 28672, 32768]
+    buckets = ps.EXHAUSTIVE_CI
     total = 0
     lo = 0
     for Ci in buckets:
@@ -283,6 +255,28 @@ def test_quant_act_exhaustive_pairs():
                                         for r, c in bad[:5]]))
             total += x.shape[0]
     assert total == 2 * amax_all.size
+
+
+@pytest.mark.parametrize("T,Ci", ps.LONG_ROW_CASES)
+def test_quant_act_long_rows(T, Ci):
+    """Rows longer than one workgroup holds in registers (amax pass, then a
+    second read): codes and scales bit-exact, with each row's largest
+    magnitude placed in a different part of the row, the last row's in the
+    last 16-byte vector."""
+    note(f"long-row quant_act T={T} Ci={Ci}")
+    rng = np.random.default_rng(Ci + T)
+    x = workloads.random_bf16(rng, T, Ci, 1.0)
+    for t in range(T):
+        # rows 0, 3, 6 (the last): inside the last 16-byte vector
+        k = Ci - 8 + t % 8 if t % 3 == 0 else int(rng.integers(0, Ci))
+        x[t, k] = workloads.f32_to_bf16_bits(np.array([(-1) ** t * (50.0 + t)], np.float32))[0]
+    qbuf = torch.full((T, Ci), 0xAB, dtype=torch.uint8, device="cuda")
+    qx, dx = sg.quant_act(bits_to_dev(x), qx=qbuf)
+    qo, do = oracle.quant_act(x)
+    assert np.array_equal(dx.cpu().numpy(), do)
+    assert np.array_equal(qx.cpu().numpy(), qo)
+    big = np.abs(workloads.bf16_bits_to_f32(x)).argmax(axis=1)
+    assert big[T - 1] >= Ci - 8 and np.all((qo[np.arange(T), big] & 0x7F) == 0x7E)
 
 
 def test_quant_weight_column_extremes():
@@ -334,12 +328,12 @@ def test_empty_and_zero_extents():
     assert sg.gemm(q1, d1, pw1).shape == (3, 0)
 
 
-@pytest.mark.parametrize("T", [70, 300])
+@pytest.mark.parametrize("T", ps.PITCHED_T)
 def test_pitched_inputs_and_outputs(T):
     """Row pitches larger than the extents (views into wider buffers); 70
     tokens run the K-split 64x64 tiles, 300 the 128-byte-step tiled kernel."""
     rng = np.random.default_rng(12)
-    Ci, Co = 528, 208
+    Ci, Co = ps.PITCHED_CI, ps.PITCHED_CO
     xb = workloads.random_bf16(rng, T, Ci + 40, 1.0)
     wb = workloads.random_bf16(rng, Ci, Co + 24, 0.02)
     xd = bits_to_dev(xb)[:, :Ci]

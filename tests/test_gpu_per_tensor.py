@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+import parity_shapes as ps
 import workloads
 from gpu_helpers import (bits_to_dev, check_close, dev_to_bits, oracle_sampled_ref,
                          packed_byte_index, sample_indices)
@@ -72,9 +73,7 @@ def check_per_tensor_quant(g, x_bits, w_bits, what):
     return qx_o, sx_o, qw_o, sw_o
 
 
-CASES = [("tiny", 16, 256, 512), ("ragged", 48, 272, 10256), ("ragged", 300, 1040, 784),
-         ("ragged", 1, 16, 16), ("8b_qkv_decode", 32, 4096, 6144),
-         ("ragged", 100, 528, 1040)]      # the K-split 64x64 tiles with scalar scales
+CASES = ps.PER_TENSOR_CASES
 
 
 @pytest.mark.parametrize("name,T,Ci,Co", CASES)

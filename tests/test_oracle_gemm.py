@@ -137,3 +137,34 @@ def test_per_token_per_channel_beats_per_tensor_on_outliers(orc):
 
     e_ptpc, e_tensor = worst_row(r["ref"]), worst_row(per_tensor)
     assert e_ptpc < 0.1 and e_tensor > 4 * e_ptpc, (e_ptpc, e_tensor)
+
+
+def test_scales_full_and_sampled_against_exact_rationals(orc):
+    """The scale step ([PTPC] §Understanding the figure: Delta_X is T x 1,
+    one per token row; Delta_W is 1 x Co, one per output column) on a
+    non-square shape with distinct scales everywhere: every reference value,
+    whole-matrix and sampled, is within double rounding of the exact rational
+    acc * Delta_X[t] * Delta_W[o] computed here from PyTorch-decoded codes.
+    A swapped row / column index or a scale taken from the wrong side fails."""
+    rng = np.random.default_rng(5)
+    T, Ci, Co = 9, 24, 5
+    qx = finite_codes(rng, (T, Ci))
+    qw = finite_codes(rng, (Ci, Co))
+    dx = (rng.uniform(0.5, 1.0, T) * 2.0 ** rng.integers(-20, 20, T)).astype(np.float32)
+    dw = (rng.uniform(0.5, 1.0, Co) * 2.0 ** rng.integers(-20, 20, Co)).astype(np.float32)
+    xv, wv = torch_decode(qx), torch_decode(qw)
+    exact = [[sum(Fraction(float(xv[t, k])) * Fraction(float(wv[k, o])) for k in range(Ci))
+              * Fraction(float(dx[t])) * Fraction(float(dw[o])) for o in range(Co)]
+             for t in range(T)]
+
+    def close(got, want):
+        return abs(Fraction(float(got)) - want) <= Fraction(2) ** -51 * abs(want)
+
+    full = orc.apply_scales(orc.gemm_exact(qx, qw), dx, dw)
+    assert full.shape == (T, Co)
+    assert all(close(full[t, o], exact[t][o]) for t in range(T) for o in range(Co))
+    rows = np.concatenate([np.arange(T), rng.integers(0, T, 40)])
+    cols = np.concatenate([np.arange(T) % Co, rng.integers(0, Co, 40)])
+    acc = orc.gemm_exact_sampled(qx, qw, rows, cols)
+    ref = orc.apply_scales_sampled(acc, rows, cols, dx, dw)
+    assert all(close(ref[i], exact[rows[i]][cols[i]]) for i in range(rows.size))

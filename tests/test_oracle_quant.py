@@ -215,3 +215,26 @@ def test_static_saturates_beyond_range(orc):
     assert q.tolist() == [[0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0xFE, 0x7E]]
     q2 = orc.quant_static(workloads.f32_to_bf16_bits(np.array([[8.0, -8.0, -0.5]], F32)), 2.0 ** -6)
     assert q2.tolist() == [[0x7E, 0xFE, 0xE0]]            # -0.5 / 2^-6 = -32 is in range
+
+
+def test_per_tensor_amax_spans_every_row_and_column(orc):
+    """Per-tensor FP8 ([PTPC] §Understanding the figure, one scalar scale for
+    the whole tensor) on a matrix whose rows all have different maxima, the
+    largest in the last row and last column: the scale is the fp32 nearest to
+    that element's magnitude / 448 (exact rationals), and every code is the
+    brute-force nearest E4M3 (ties to even) of the IEEE fp32 quotient.  An
+    amax that reads only some rows or columns gives another scale and fails."""
+    from test_oracle_codec import brute_force_encode
+    rng = np.random.default_rng(9)
+    R, C = 37, 48
+    v = rng.standard_normal((R, C)).astype(F32)
+    v *= (1.0 + np.arange(R, dtype=F32)[:, None] / 4)          # row maxima differ
+    v[R - 1, C - 1] = -300.5                                    # the tensor's largest
+    x = workloads.f32_to_bf16_bits(v)
+    xf = f32(x)
+    assert np.abs(xf).argmax() == R * C - 1
+    q, d = orc.quant_tensor(x)
+    want_d = nearest_f32(Fraction(float(np.abs(xf).max())) / 448)
+    assert d == want_d
+    assert q[R - 1, C - 1] == 0xFE
+    assert np.array_equal(q, brute_force_encode((xf / np.float32(d)).astype(F32)))
