@@ -153,6 +153,28 @@ ptpc_status ptpc_gemm_ws(const uint8_t* qx, int64_t ldq, const float* dx,
                          int64_t Ci, int64_t Co, void* out, int64_t ldo,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ptpc_gemm_ws for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels and the same result, bit for bit, as ptpc_gemm_ws with a
+ * workspace, but the split-K partial sums go to a scratch array the library
+ * holds on each GPU (PTPC_NOALLOC_SCRATCH_BYTES, kept until the process
+ * ends) and nothing is allocated or freed.  The caller still passes inputs
+ * and outputs; the stream must belong to the current device.  Where
+ * ptpc_gemm_workspace_bytes(T, Ci, Co) is 0 this is exactly ptpc_gemm.
+ * Shapes whose split needs more than PTPC_NOALLOC_SCRATCH_BYTES return
+ * PTPC_ERR_UNSUPPORTED before anything is launched (the current split plan
+ * never needs more: at most 16 MiB by construction).  Calls that overlap on
+ * one GPU (different streams, or threads) share the scratch and race; calls
+ * in one stream are ordered and safe.  The first call on a device looks up
+ * the scratch's device address (PTPC_ERR_HIP if that fails).
+ */
+#define PTPC_NOALLOC_SCRATCH_BYTES (16u << 20)
+ptpc_status ptpc_gemm_noalloc(const uint8_t* qx, int64_t ldq, const float* dx,
+                              const void* w_packed, const float* dw, int64_t T,
+                              int64_t Ci, int64_t Co, void* out, int64_t ldo,
+                              void* stream);
+
 /* Workspace needed by ptpc_gemm_unfused: 4 * T * Co bytes (fp32 [T x Co]). */
 size_t ptpc_gemm_unfused_workspace_bytes(int64_t T, int64_t Co);
 

@@ -26,7 +26,7 @@ _STATUS = {
 EXPORTS = (
     "ptpc_status_string", "ptpc_abi_version", "ptpc_quant_act", "ptpc_weight_packed_bytes",
     "ptpc_quant_weight", "ptpc_unpack_weight", "ptpc_gemm",
-    "ptpc_gemm_workspace_bytes", "ptpc_gemm_ws",
+    "ptpc_gemm_workspace_bytes", "ptpc_gemm_ws", "ptpc_gemm_noalloc",
     "ptpc_gemm_unfused_workspace_bytes", "ptpc_gemm_unfused",
     "ptpc_gemm_unfused_bf16_workspace_bytes", "ptpc_gemm_unfused_bf16", "ptpc_tensor_scale",
     "ptpc_quant_act_static", "ptpc_quant_weight_static", "ptpc_gemm_tensor",
@@ -73,6 +73,8 @@ def lib():
         L.ptpc_gemm_workspace_bytes.argtypes = [I, I, I]
         L.ptpc_gemm_ws.restype = ctypes.c_int
         L.ptpc_gemm_ws.argtypes = [P, I, P, P, P, I, I, I, P, I, P, S, P]
+        L.ptpc_gemm_noalloc.restype = ctypes.c_int
+        L.ptpc_gemm_noalloc.argtypes = [P, I, P, P, P, I, I, I, P, I, P]
         L.ptpc_gemm_unfused_bf16_workspace_bytes.restype = S
         L.ptpc_gemm_unfused_bf16_workspace_bytes.argtypes = [I, I]
         L.ptpc_gemm_unfused_bf16.restype = ctypes.c_int
@@ -269,6 +271,22 @@ def gemm_ws(qx, dx, pw: PackedWeight, out=None, workspace=None, stream=None):
     _check("ptpc_gemm_ws", lib().ptpc_gemm_ws(_ptr(qx), ldq, _ptr(dx), _ptr(pw.data), _ptr(pw.dw),
                                               T, Ci, pw.Co, _ptr(out), ldo, _ptr(workspace),
                                               nbytes, _stream(stream)))
+    return out
+
+
+# Scratch bytes the library holds per GPU for gemm_noalloc (include/ptpc.h).
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def gemm_noalloc(qx, dx, pw: PackedWeight, out=None, stream=None):
+    """ptpc_gemm_noalloc: gemm_ws without a workspace -- the split-K partials
+    go to the library's own per-GPU scratch, nothing is allocated (pass `out`
+    to allocate nothing here either).  Calls overlapping on one GPU race."""
+    T, Ci, ldq, out = _gemm_args(qx, dx, pw, out, per_tensor=False)
+    ldo = max(out.stride(0), out.shape[1])
+    _check("ptpc_gemm_noalloc",
+           lib().ptpc_gemm_noalloc(_ptr(qx), ldq, _ptr(dx), _ptr(pw.data), _ptr(pw.dw), T, Ci,
+                                   pw.Co, _ptr(out), ldo, _stream(stream)))
     return out
 
 

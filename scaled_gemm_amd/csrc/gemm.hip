@@ -38,6 +38,7 @@
 // gemm_decode_kernel (up to 64 tokens: K split across the waves of a
 // workgroup, operands loaded straight into registers), and the second
 // passes of the two-step forms and of split-K.
+#include <mutex>
 #include <utility>
 
 #include "device_common.h"
@@ -1583,6 +1584,36 @@ hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, c
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)rescale_blocks(T, Co)), dim3(256), 0,
                        s, ws, splits, dx, dw, T, Co, out, ldo);
     return hipGetLastError();
+}
+
+// Scratch of ptpc_gemm_noalloc (for callers that cannot allocate): the fp32
+// partial sums of the split-K form live in this file-scope device array
+// instead of a caller workspace.  Each GPU holds its own copy for the life of
+// the process.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in, not a device address): the device address is
+// looked up once per device with hipGetSymbolAddress, with that device
+// current, and kept.  Every split range writes its whole slice, so nothing
+// needs clearing between calls; calls that overlap on one GPU share the
+// array and race.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_gemm_unfused_bf16(const uint8_t* qx, int64_t ldq, const float* dx,

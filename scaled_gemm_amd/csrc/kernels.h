@@ -78,4 +78,10 @@ hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, c
                               const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                               int64_t ldo, float* ws, int splits, hipStream_t s);
 
+// The no-allocation split-K form: its scratch size, and the device address
+// of the current device's copy of the scratch array (looked up once per
+// device).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace ptpc

@@ -185,6 +185,27 @@ ptpc_status ptpc_gemm_ws(const uint8_t* qx, int64_t ldq, const float* dx, const 
         ptpc::gemm_splitk_plan(T, Ci, Co), as_stream(stream)));
 }
 
+ptpc_status ptpc_gemm_noalloc(const uint8_t* qx, int64_t ldq, const float* dx,
+                              const void* w_packed, const float* dw, int64_t T, int64_t Ci,
+                              int64_t Co, void* out, int64_t ldo, void* stream) {
+    static_assert(PTPC_NOALLOC_SCRATCH_BYTES == ptpc::kNoAllocScratchBytes, "scratch size");
+    ptpc_status st = check_gemm(qx, ldq, dx, w_packed, dw, T, Ci, Co, out, ldo);
+    if (st != PTPC_OK || T == 0 || Co == 0) return st;
+    const size_t need = ptpc_gemm_workspace_bytes(T, Ci, Co);
+    if (need > ptpc::kNoAllocScratchBytes) return PTPC_ERR_UNSUPPORTED;
+    if (forced_launch_failure()) return PTPC_ERR_HIP;
+    if (need == 0)
+        return from_hip(ptpc::launch_gemm(qx, ldq, dx, static_cast<const uint8_t*>(w_packed), dw,
+                                          T, Ci, Co, static_cast<uint16_t*>(out), ldo, nullptr,
+                                          as_stream(stream)));
+    void* ws = nullptr;
+    if (ptpc::noalloc_scratch(&ws) != hipSuccess) return PTPC_ERR_HIP;
+    return from_hip(ptpc::launch_gemm_splitk(
+        qx, ldq, dx, static_cast<const uint8_t*>(w_packed), dw, T, Ci, Co,
+        static_cast<uint16_t*>(out), ldo, static_cast<float*>(ws),
+        ptpc::gemm_splitk_plan(T, Ci, Co), as_stream(stream)));
+}
+
 size_t ptpc_gemm_unfused_bf16_workspace_bytes(int64_t T, int64_t Co) {
     if (T <= 0 || Co <= 0 || T > kMaxExtent || Co > kMaxExtent || T * Co > kMaxOutputs) return 0;
     return (size_t)T * (size_t)Co * 2;

@@ -124,6 +124,11 @@ hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, c
     return hipSuccess;
 }
 
+hipError_t noalloc_scratch(void** ptr) {
+    *ptr = reinterpret_cast<void*>(uintptr_t(0x900000));
+    return hipSuccess;
+}
+
 }  // namespace ptpc
 
 // Fake device addresses: never dereferenced (the stubs only look at them).
@@ -226,8 +231,12 @@ int main() {
                         st = ptpc_gemm_ws(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo,
                                           P3 + 0x10000, need, nullptr);
                         check(st, n0, empty);
+                        n0 = g_launches;
+                        st = ptpc_gemm_noalloc(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, nullptr);
+                        check(st, n0, empty);
+                        if (st == PTPC_OK) REQUIRE(need <= PTPC_NOALLOC_SCRATCH_BYTES);
                         (void)ptpc_gemm_kernel(T, Ci, Co);
-                        calls += 5;
+                        calls += 6;
                     }
     std::printf("abi_fuzz: %ld calls, %ld launches, %ld failures\n", calls, g_launches, g_fail);
     return g_fail == 0 ? 0 : 1;

@@ -193,9 +193,26 @@ r = [L.ptpc_quant_act(A, 4, 256, 256, B, 256, C, None),
      L.ptpc_gemm_tensor(A, 256, B, C, D, 4, 256, 512, E, 512, None),
      L.ptpc_gemm_unfused_bf16(A, 256, B, C, D, 4, 256, 512, E, 512, D, None),
      L.ptpc_gemm_ws(A, 8192, B, C, D, 128, 8192, 10240, E, 10240, D, 1 << 30, None),
+     L.ptpc_gemm_noalloc(A, 8192, B, C, D, 128, 8192, 10240, E, 10240, None),
      L.ptpc_quant_act(A, 0, 256, 256, B, 256, C, None)]
 print(r)
-assert r == [5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 0], r
+assert r == [5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 0], r
 """ % ROOT
     env = dict(os.environ, PTPC_FAULT="launch", HIP_VISIBLE_DEVICES="")
     subprocess.run(["python", "-c", code], check=True, env=env)
+
+
+def test_noalloc_scratch_covers_every_split(L):
+    """ptpc_gemm_noalloc's per-GPU scratch holds the partial sums of every
+    shape the split-K plan splits (16 MiB by construction), and the call
+    validates like ptpc_gemm (no compute call here)."""
+    import scaled_gemm_amd as sg
+    assert sg.NOALLOC_SCRATCH_BYTES == 16 << 20
+    worst = max(L.ptpc_gemm_workspace_bytes(T, Ci, Co) for T in range(65, 256)
+                for Ci in (2048, 8192, 28672) for Co in range(16, 66000, 16))
+    assert 0 < worst <= sg.NOALLOC_SCRATCH_BYTES
+    f = L.ptpc_gemm_noalloc
+    assert f(A, 256, B, C, D, 0, 256, 512, E, 512, None) == 0
+    assert f(A, 256, B, C, D, 4, 256, 500, E, 512, None) == 3
+    assert f(NULL, 256, B, C, D, 4, 256, 512, E, 512, None) == 1
+    assert f(A, 256, B, C, D, 4, 256, 512, E, 516, None) == 4
