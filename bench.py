@@ -8,15 +8,23 @@ quantization, the fused FP8 GEMM, and the two-step (unfused) GEMM.  Each
 stage is bracketed by HIP events on the stream it runs on, so per-kernel
 averages come from the timed region itself.
 
+Every timing rotates over several copies of the inputs at distinct
+addresses, more than 768 MiB in all, so that no stage finds its input in
+the GPU's 256 MB memory-side cache from an earlier repetition: what the
+HBM figures measure is HBM.
+
 Prints one JSON line.  `value` is whole-step throughput: the FP8 contraction
 work of the step (two GEMMs, 2*T*Ci*Co flops each) divided by the step time.
 `roofline` is the fused GEMM against the dense FP8 MFMA peak; `quant_act`
-carries the activation quantizer against HBM bandwidth; `cpu_baseline` is
-the CPU oracle on a bounded sample of the same workload.
+carries the activation quantizer against HBM bandwidth; `comparison` holds
+the other forms timed in interleaved rounds; `judged_shapes` the fused GEMM
+and the activation quantizer on the other large layer shapes; `cpu_baseline`
+is the CPU oracle on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -26,10 +34,22 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (no sparsity)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fused_70b_down_traffic.json")
+ROTATE_BYTES = 768 << 20      # rotated input bytes: three times the 256 MB memory-side cache
+MAX_SETS = 64
+
+# HBM-traffic records (rocprofv3 FETCH_SIZE / WRITE_SIZE of one kernel on
+# the default workload), valid only while the kernel's code is unchanged.
+TRAFFIC = {
+    "gemm_fused": {"file": "gemm_fused_70b_down_traffic.json",
+                   "sources": ("gemm.hip", "device_common.h"),
+                   "kernel": "gemm16_kernel<256, 256, 2, 2, true>"},
+    "quant_act": {"file": "quant_act_70b_down_traffic.json",
+                  "sources": ("quant.hip", "device_common.h"),
+                  "kernel": "quant_act_kernel<256, 16>"},
+}
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
@@ -39,10 +59,14 @@ def parse():
     p.add_argument("--layer", default=None, help="70b_sweep layer")
     p.add_argument("--T", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-judged", action="store_true",
+                   help="skip the per-shape lines of the other large layer shapes")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--only", default=None,
                    help="comma list of stages to run (profiling); default all")
+    p.add_argument("--judged-only", default=None,
+                   help="profiling: run only the judged shapes whose names contain this text")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="run a plain device copy of this many MiB (3x) before timing, "
                         "as the reference kernel for HBM byte counters")
@@ -58,18 +82,22 @@ def parse():
                         "quant_act GB/s, fused / two-step GEMM TFLOP/s; not the bench line")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
-                        "--only gemm_fused --copy-calibration-mb run into the traffic record "
-                        "and exit (no GPU needed)")
-    return p.parse_args()
+                        "--only <kernel> --copy-calibration-mb run into the traffic record of "
+                        "--traffic-kernel and exit (no GPU needed)")
+    p.add_argument("--traffic-kernel", default="gemm_fused", choices=sorted(TRAFFIC))
+    return p.parse_args(argv)
 
 
-def gemm_source_hash():
-    """Hash of the GEMM's code: gemm.hip and the device header it includes,
-    with comments and blank space removed, so that the traffic record stays
-    valid across comment edits and is dropped on any code change."""
+# ---------------------------------------------------------------------------
+# HBM traffic records
+# ---------------------------------------------------------------------------
+def source_hash(kind):
+    """Hash of a kernel's code (its sources with comments and blank space
+    removed), so that a traffic record stays valid across comment edits and
+    is dropped on any code change."""
     import re
     text = ""
-    for name in ("gemm.hip", "device_common.h"):
+    for name in TRAFFIC[kind]["sources"]:
         with open(os.path.join(ROOT, "scaled_gemm_amd", "csrc", name)) as f:
             text += f.read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -78,24 +106,30 @@ def gemm_source_hash():
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per fused-GEMM launch from rocprofv3 FETCH_SIZE/WRITE_SIZE,
-    only if the counters were taken on the current kernel source."""
+def traffic_file(kind):
+    return os.path.join(ROOT, "profiles", TRAFFIC[kind]["file"])
+
+
+def measured_traffic(workload, kind):
+    """HBM bytes per launch of `kind` from rocprofv3 FETCH_SIZE/WRITE_SIZE,
+    only if the counters were taken on this workload and the current code."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kind)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("workload") != workload or t.get("gemm_source_sha256_16") != gemm_source_hash():
+    if t.get("workload") != workload or t.get("source_sha256_16") != source_hash(kind):
         return None
     return t.get("bytes_per_launch")
 
 
-def traffic_record(fetch_csv, write_csv, workload, copy_mb):
-    """HBM bytes per fused-GEMM launch: the FETCH_SIZE / WRITE_SIZE counters
-    (KiB per dispatch) of the GEMM, each scaled by the ratio of the known
-    bytes of a plain device copy to what the same counter reads for it."""
+def traffic_record(fetch_csv, write_csv, workload, copy_mb, kind):
+    """HBM bytes per launch: the FETCH_SIZE / WRITE_SIZE counters (KiB per
+    dispatch) of the kernel, each scaled by the ratio of the known bytes of a
+    plain device copy to what the same counter reads for it."""
     import csv
+
+    match = TRAFFIC[kind]["kernel"]
 
     def per_kernel(path, counter):
         vals = {}
@@ -104,8 +138,7 @@ def traffic_record(fetch_csv, write_csv, workload, copy_mb):
                 if r["Counter_Name"] != counter:
                     continue
                 name = r["Kernel_Name"]
-                key = ("gemm" if "gemm16_kernel<256, 256, 2, 2, true>" in name
-                       else "copy" if "copyBuffer" in name else None)
+                key = "kernel" if match in name else "copy" if "copyBuffer" in name else None
                 if key:
                     vals.setdefault(key, []).append(float(r["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in vals.items()}
@@ -115,30 +148,33 @@ def traffic_record(fetch_csv, write_csv, workload, copy_mb):
     copy_bytes = float(copy_mb) * (1 << 20)
     f_factor = copy_bytes / (f["copy"] * 1024.0)
     w_factor = copy_bytes / (w["copy"] * 1024.0)
-    fetch = f["gemm"] * 1024.0 * f_factor
-    write = w["gemm"] * 1024.0 * w_factor
-    return {"workload": workload, "gemm_source_sha256_16": gemm_source_hash(),
-            "kernel": "gemm16_kernel<256, 256, 2, 2, true> (fused, this workload's tiles)",
-            "fetch_kib_raw": f["gemm"], "write_kib_raw": w["gemm"],
+    fetch = f["kernel"] * 1024.0 * f_factor
+    write = w["kernel"] * 1024.0 * w_factor
+    prof = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {{c}} --output-format csv "
+            f"-d $REPO/gpurun_out/prof_{{d}} -o p -- python -u $REPO/bench.py --steps 3 "
+            f"--warmup 1 --no-cpu-baseline --no-judged --only {kind} "
+            f"--copy-calibration-mb {copy_mb}")
+    return {"workload": workload, "source_sha256_16": source_hash(kind),
+            "kernel": f"{match} ({kind}, this workload's launch)",
+            "fetch_kib_raw": f["kernel"], "write_kib_raw": w["kernel"],
             "copy_bytes": copy_bytes, "copy_fetch_kib_raw": f["copy"],
             "copy_write_kib_raw": w["copy"], "fetch_factor": f_factor,
             "write_factor": w_factor, "fetch_bytes": fetch, "write_bytes": write,
             "bytes_per_launch": fetch + write,
             "commands": [
-                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
-                "-d $REPO/gpurun_out/prof_fetch -o p -- python -u $REPO/bench.py --steps 3 "
-                f"--warmup 1 --no-cpu-baseline --only gemm_fused --copy-calibration-mb {copy_mb}",
-                "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv "
-                "-d $REPO/gpurun_out/prof_write -o p -- python -u $REPO/bench.py --steps 3 "
-                f"--warmup 1 --no-cpu-baseline --only gemm_fused --copy-calibration-mb {copy_mb}",
+                prof.format(c="FETCH_SIZE", d="fetch"), prof.format(c="WRITE_SIZE", d="write"),
                 "python bench.py --traffic-from $REPO/gpurun_out/prof_fetch/p_counter_collection.csv "
-                f"$REPO/gpurun_out/prof_write/p_counter_collection.csv --copy-calibration-mb {copy_mb}"],
-            "note": ("Counters in KiB per dispatch, averaged over the fused-GEMM launches; each "
-                     "scaled by known copy bytes / counter reading for a device copy of "
-                     f"{copy_mb} MiB (torch copy_) in the same run. On MI355X FETCH_SIZE reads "
-                     "about half of the copy's bytes, WRITE_SIZE all of them.")}
+                f"$REPO/gpurun_out/prof_write/p_counter_collection.csv --copy-calibration-mb "
+                f"{copy_mb} --traffic-kernel {kind}"],
+            "note": ("Counters in KiB per dispatch, averaged over the kernel's launches (inputs "
+                     "rotating over copies larger than the memory-side cache); each scaled by "
+                     "known copy bytes / counter reading for a device copy of "
+                     f"{copy_mb} MiB (torch copy_) in the same run.")}
 
 
+# ---------------------------------------------------------------------------
+# CPU baseline
+# ---------------------------------------------------------------------------
 def cpu_baseline(x_bits, w_bits, target_s):
     """The CPU oracle (as it stands) on the first R token rows with the whole
     weight: quantize, contract exactly, scale.  The oracle spreads rows over
@@ -166,12 +202,15 @@ def cpu_baseline(x_bits, w_bits, target_s):
         t_g = rows(R)
     total = t_w + t_g
     flops = 2.0 * R * Ci * Co
+    nproc = os.cpu_count()
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else nproc
     return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": min(nthr, R),
-            "kind": "oracle",
+            "kind": "oracle", "nproc": nproc, "cpus_available": affinity,
             "sample": (f"first {R} token rows of the workload with its whole weight: "
                        f"quant_weight [{Ci}x{Co}] + quant_act [{R}x{Ci}] + exact GEMM "
                        f"[{R}x{Ci}]x[{Ci}x{Co}] + scales; {total:.1f} s wall "
-                       f"(weight quantization {t_w:.1f} s); {nthr} OpenMP threads")}
+                       f"(weight quantization {t_w:.1f} s); {nthr} OpenMP threads, "
+                       f"nproc {nproc}, {affinity} CPUs available to the process")}
 
 
 def no_nan(v):
@@ -185,11 +224,72 @@ def no_nan(v):
     return v
 
 
-def act_bytes_ref(T, Ci):
-    """Bytes a bf16 -> 1-byte cast of a [T x Ci] matrix moves."""
-    return 3.0 * T * Ci
+def act_bytes(T, Ci):
+    """Algorithmic bytes of the activation quantizer: 2 read + 1 written per
+    element, 4 per row scale."""
+    return 3.0 * T * Ci + 4.0 * T
 
 
+def gemm_min_bytes(T, Ci, Co):
+    return T * Ci + Ci * Co + 2.0 * T * Co + 4.0 * (T + Co)
+
+
+def round_k(Ci):
+    """K extent of the packed weight (whole 128-byte K tiles)."""
+    return (Ci + 127) // 128 * 128
+
+
+def n_sets(set_bytes):
+    """Input copies to rotate over so that more than ROTATE_BYTES pass
+    between two uses of one copy (at least 3)."""
+    return int(min(MAX_SETS, max(3, math.ceil(ROTATE_BYTES / max(set_bytes, 1)) + 2)))
+
+
+def batch_ms(launch, n, stream):
+    """Per-launch time of n back-to-back launches between one HIP event pair
+    on `stream`; launch(i) issues repetition i (on input copy i mod sets)."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for i in range(n):
+        launch(i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / n
+
+
+def graph_ms(launch, n, stream, replays=5):
+    """Per-launch time of n launches captured once in a HIP graph and
+    replayed: the GPU time of short kernels without the host's per-call cost
+    (launch(i) issues repetition i on input copy i mod sets; nothing the
+    captured calls launch clears memory with a memset).  Median over replays,
+    each between its own event pair on `stream`."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(n):
+                launch(i)
+    stream.wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(replays):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        g.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        t.append(ev[0].elapsed_time(ev[1]) / n)
+    del g
+    return sorted(t)[len(t) // 2]
+
+
+# ---------------------------------------------------------------------------
+# model-scale load time, hipBLASLt context, sweep
+# ---------------------------------------------------------------------------
 def model_load(args):
     """Load-time weight quantization at model scale: each of the 80 decoder
     layers' four linear weights is drawn in bf16 on the GPU, quantized per
@@ -313,10 +413,11 @@ def scaled_mm_context(args):
 
 
 def sweep(args):
-    """Per-shape kernel rates over every workload shape (after a warm-up, three
-    interleaved rounds over the stages, each round one HIP event pair on the
-    launch stream around `steps` back-to-back launches; the best round per
-    stage)."""
+    """Per-shape kernel rates over every workload shape.  After a warm-up,
+    three interleaved rounds over the stages, each round one HIP event pair
+    on the launch stream around back-to-back launches that rotate over
+    copies of the inputs (more than 768 MiB between two uses of a copy); the
+    best round per stage."""
     import numpy as np
     import torch
 
@@ -336,70 +437,146 @@ def sweep(args):
         else:
             shape, x_bits, w_bits = workloads.make(name)
         T, Ci, Co = shape.T, shape.Ci, shape.Co
-        x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-        w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        w0 = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
         del x_bits, w_bits
-        pw = sg.quant_weight(w)
-        qx, dx = sg.quant_act(x)
+        pw0 = sg.quant_weight(w0)
+        qx0, dx0 = sg.quant_act(x0)
+        n = n_sets(T * Ci + pw0.data.numel())
+        nx = n_sets(2 * T * Ci)
+        xs = [x0] + [x0.clone() for _ in range(nx - 1)]
+        qxs = [qx0] + [qx0.clone() for _ in range(max(n, nx) - 1)]
+        dxs = [dx0] + [dx0.clone() for _ in range(max(n, nx) - 1)]
+        pws = [pw0] + [sg.PackedWeight(pw0.data.clone(), pw0.dw.clone(), Ci, Co)
+                       for _ in range(n - 1)]
+        ws_ = [w0] + [w0.clone() for _ in range(2)]
+        sx_t = sg.tensor_scale(x0)
+        pw_t = sg.quant_weight_static(w0, sg.tensor_scale(w0))
+        pwts = [pw_t] + [sg.PackedWeight(pw_t.data.clone(), pw_t.dw, Ci, Co, per_tensor=True)
+                         for _ in range(n - 1)]
         out = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
-        out2 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
         ws = torch.empty((T, Co), dtype=torch.float32, device=dev)
         ws16 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
         gws = torch.empty((max(1, sg.gemm_workspace_bytes(T, Ci, Co)),), dtype=torch.uint8,
                           device=dev)
-        sx_t = sg.tensor_scale(x)
-        pw_t = sg.quant_weight_static(w, sg.tensor_scale(w))
         calls = {
-            "quant_weight": lambda: sg.quant_weight(w, out=pw),
-            "quant_act": lambda: sg.quant_act(x, qx=qx, dx=dx),
-            "gemm_fused": lambda: sg.gemm(qx, dx, pw, out=out),
-            "gemm_unfused": lambda: sg.gemm_unfused(qx, dx, pw, out=out2, workspace=ws),
-            "gemm_unfused_bf16": lambda: sg.gemm_unfused_bf16(qx, dx, pw, out=out2,
-                                                              workspace=ws16),
-            "gemm_tensor": lambda: sg.gemm_tensor(qx, sx_t, pw_t, out=out2),
-            "gemm_ws": lambda: sg.gemm_ws(qx, dx, pw, out=out2, workspace=gws),
+            "quant_weight": lambda i: sg.quant_weight(ws_[i % 3], out=pws[i % n]),
+            "quant_act": lambda i: sg.quant_act(xs[i % nx], qx=qxs[i % nx], dx=dxs[i % nx]),
+            "gemm_fused": lambda i: sg.gemm(qxs[i % n], dxs[i % n], pws[i % n], out=out),
+            "gemm_unfused": lambda i: sg.gemm_unfused(qxs[i % n], dxs[i % n], pws[i % n],
+                                                      out=out, workspace=ws),
+            "gemm_unfused_bf16": lambda i: sg.gemm_unfused_bf16(qxs[i % n], dxs[i % n],
+                                                                pws[i % n], out=out,
+                                                                workspace=ws16),
+            "gemm_tensor": lambda i: sg.gemm_tensor(qxs[i % n], sx_t, pwts[i % n], out=out),
+            "gemm_ws": lambda i: sg.gemm_ws(qxs[i % n], dxs[i % n], pws[i % n], out=out,
+                                            workspace=gws),
         }
-        # Three interleaved rounds over the stages, each stage's best round
-        # reported: a stage timed in one block right after another reads the
-        # clock's settling (short launches by up to 20%).
         for fn in calls.values():
-            for _ in range(max(3, args.warmup)):
-                fn()
+            for i in range(max(3, args.warmup)):
+                fn(i)
         rounds = {k: [] for k in calls}
+        reps = max(args.steps, 2 * max(n, nx))
         for _ in range(3):
             for k, fn in calls.items():
-                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                ev[0].record(stream)
-                for i in range(args.steps):
-                    fn()
-                ev[1].record(stream)
-                torch.cuda.synchronize()
-                rounds[k].append(ev[0].elapsed_time(ev[1]) / args.steps)
+                rounds[k].append(batch_ms(fn, reps, stream))
         ms = {k: min(v) for k, v in rounds.items()}
         flops = 2.0 * T * Ci * Co
-        act_b = 3.0 * T * Ci + 4.0 * T
+        ab = act_bytes(T, Ci)
         print(json.dumps({
             "workload": shape.name, "T": T, "Ci": Ci, "Co": Co,
+            "gemm_kernel": sg.gemm_kernel(T, Ci, Co), "input_copies": n,
             "ms": {k: round(v, 4) for k, v in ms.items()},
             "gemm_fused_tflops": round(flops / ms["gemm_fused"] / 1e9, 1),
             "gemm_fused_frac_fp8_peak": round(flops / ms["gemm_fused"] / 1e9 / PEAK_FP8_TFLOPS, 4),
-            "gemm_fused_gbs_min_bytes": round((T * Ci + Ci * Co + 2.0 * T * Co + 4.0 * (T + Co))
-                                              / ms["gemm_fused"] / 1e6, 1),
+            "gemm_fused_gbs_min_bytes": round(gemm_min_bytes(T, Ci, Co) / ms["gemm_fused"] / 1e6, 1),
             "gemm_unfused_tflops": round(flops / ms["gemm_unfused"] / 1e9, 1),
             "fused_over_unfused": round(ms["gemm_unfused"] / ms["gemm_fused"], 3),
             "fused_over_unfused_bf16": round(ms["gemm_unfused_bf16"] / ms["gemm_fused"], 3),
             "ptpc_over_per_tensor_gemm": round(ms["gemm_fused"] / ms["gemm_tensor"], 3),
             "gemm_ws_speedup": round(ms["gemm_fused"] / ms["gemm_ws"], 3),
-            "gemm_ws_gbs_min_bytes": round((T * Ci + Ci * Co + 2.0 * T * Co + 4.0 * (T + Co))
-                                           / ms["gemm_ws"] / 1e6, 1),
-            "quant_act_gbs": round(act_b / ms["quant_act"] / 1e6, 1),
-            "quant_act_frac_hbm": round(act_b / ms["quant_act"] / 1e6 / PEAK_HBM_GBS, 4),
+            "gemm_ws_gbs_min_bytes": round(gemm_min_bytes(T, Ci, Co) / ms["gemm_ws"] / 1e6, 1),
+            "quant_act_gbs": round(ab / ms["quant_act"] / 1e6, 1),
+            "quant_act_frac_hbm": round(ab / ms["quant_act"] / 1e6 / PEAK_HBM_GBS, 4),
             "quant_weight_gbs": round((3.0 * Ci * Co + 4.0 * Co) / ms["quant_weight"] / 1e6, 1),
         }), flush=True)
-        del x, w, pw, qx, dx, out, out2, ws, ws16, sx_t, pw_t, gws
+        del x0, w0, xs, qxs, dxs, pws, ws_, pwts, pw_t, sx_t, out, ws, ws16, gws, calls
         torch.cuda.empty_cache()
 
 
+# ---------------------------------------------------------------------------
+# the judged shapes: the other large layers the targets are quoted on
+# ---------------------------------------------------------------------------
+def judged_shapes(stream, only=None):
+    """The fused GEMM and the activation quantizer on the 70B layers at 1024
+    and 8192 tokens and the 8B gate_up layer, inputs drawn on the GPU with
+    the workloads' value structure.  Each figure: after a warm-up, five rounds
+    of launches between one HIP event pair, rotating over input copies (more
+    than 768 MiB between two uses of a copy); the median round.  The GEMM's
+    rounds are back-to-back launches; the activation quantizer's (3-130 us
+    kernels, shorter than the host's per-call cost at the smaller shapes)
+    replay the launches captured in a HIP graph."""
+    import torch
+
+    import scaled_gemm_amd as sg
+    import workloads
+
+    dev = torch.device("cuda:0")
+    shapes = [("8b_gate_up", 2048, 4096, 28672, "outlier_normal", 0.02)]
+    shapes += [(f"70b_{layer}", T, Ci, Co, "student_lognormal", 0.01)
+               for layer, (Ci, Co) in workloads.SWEEP_LAYERS.items() for T in (1024, 8192)]
+    res = []
+    for k, (name, T, Ci, Co, kind, sigma) in enumerate(shapes):
+        if only and only not in f"{name}_T{T}":
+            continue
+        x = workloads.device_activation(kind, T, Ci, 7000 + k, dev)
+        w = workloads.device_weight(100, k, Ci, Co, sigma, dev)
+        pw = sg.quant_weight(w)
+        del w
+        qx, dx = sg.quant_act(x)
+        n = n_sets(T * Ci + pw.data.numel())
+        nx = n_sets(2 * T * Ci)
+        pws = [pw] + [sg.PackedWeight(pw.data.clone(), pw.dw.clone(), Ci, Co) for _ in range(n - 1)]
+        qxs = [qx] + [qx.clone() for _ in range(max(n, nx) - 1)]
+        dxs = [dx] + [dx.clone() for _ in range(max(n, nx) - 1)]
+        xs = [x] + [x.clone() for _ in range(nx - 1)]
+        out = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
+
+        def gemm(i):
+            sg.gemm(qxs[i % n], dxs[i % n], pws[i % n], out=out)
+
+        def act(i):
+            sg.quant_act(xs[i % nx], qx=qxs[i % nx], dx=dxs[i % nx])
+
+        for i in range(3 * n):
+            gemm(i)
+        for i in range(2 * nx):
+            act(i)
+        reps_g = max(2 * n, 10)
+        reps_a = max(2 * nx, 20)
+        g_ms = sorted(batch_ms(gemm, reps_g, stream) for _ in range(5))[2]
+        a_ms = graph_ms(act, reps_a, stream)
+        flops = 2.0 * T * Ci * Co
+        res.append({
+            "shape": f"{name}_T{T}", "T": T, "Ci": Ci, "Co": Co,
+            "gemm_kernel": sg.gemm_kernel(T, Ci, Co),
+            "gemm_ms": round(g_ms, 4), "gemm_tflops": round(flops / g_ms / 1e9, 1),
+            "gemm_frac_fp8_peak": round(flops / g_ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "quant_act_ms": round(a_ms, 4),
+            "quant_act_gbs": round(act_bytes(T, Ci) / a_ms / 1e6, 1),
+            "quant_act_frac_hbm": round(act_bytes(T, Ci) / a_ms / 1e6 / PEAK_HBM_GBS, 4),
+            "input_copies": {"gemm": n, "quant_act": nx},
+        })
+        print(f"# judged {name} T={T}: gemm {res[-1]['gemm_frac_fp8_peak']:.3f} of FP8 peak, "
+              f"quant_act {res[-1]['quant_act_frac_hbm']:.3f} of HBM", file=sys.stderr, flush=True)
+        del x, pw, qx, dx, pws, qxs, dxs, xs, out
+        torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# the bench line
+# ---------------------------------------------------------------------------
 def main():
     args = parse()
     if args.gpus != 1:
@@ -418,8 +595,8 @@ def main():
         return
     if args.traffic_from:
         rec = traffic_record(args.traffic_from[0], args.traffic_from[1], args.workload,
-                             args.copy_calibration_mb or 1024)
-        with open(TRAFFIC_FILE, "w") as f:
+                             args.copy_calibration_mb or 1024, args.traffic_kernel)
+        with open(traffic_file(args.traffic_kernel), "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
         print(json.dumps(rec, indent=1))
@@ -435,6 +612,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sg.lib()
+    stream = torch.cuda.current_stream()
+
+    if args.judged_only:
+        print(json.dumps(judged_shapes(stream, args.judged_only)), flush=True)
+        return
 
     if args.workload == "70b_sweep":
         shape, x_bits, w_bits = workloads.make("70b_sweep", T=args.T or 8192,
@@ -442,18 +624,24 @@ def main():
     else:
         shape, x_bits, w_bits = workloads.make(args.workload, T=args.T)
     T, Ci, Co = shape.T, shape.Ci, shape.Co
-    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    w0 = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # outputs allocated once, outside the timed region
-    qx = torch.empty((T, Ci), dtype=torch.uint8, device=dev)
-    dx = torch.empty((T,), dtype=torch.float32, device=dev)
-    pw = sg.PackedWeight(torch.empty((sg.packed_bytes(Ci, Co),), dtype=torch.uint8, device=dev),
-                         torch.empty((Co,), dtype=torch.float32, device=dev), Ci, Co)
+    # Input copies at distinct addresses; step k works on copy k mod n, so
+    # every stage reads inputs no repetition touched for n - 1 steps (more
+    # than 768 MiB of other data in between).  Outputs are written, not read,
+    # and are shared.
+    n = n_sets(min(2 * T * Ci, T * Ci + Co * round_k(Ci)))
+    xs = [x0] + [x0.clone() for _ in range(n - 1)]
+    wts = [w0] + [w0.clone() for _ in range(n - 1)]
+    qxs = [torch.empty((T, Ci), dtype=torch.uint8, device=dev) for _ in range(n)]
+    dxs = [torch.empty((T,), dtype=torch.float32, device=dev) for _ in range(n)]
+    pws = [sg.PackedWeight(torch.empty((sg.packed_bytes(Ci, Co),), dtype=torch.uint8, device=dev),
+                           torch.empty((Co,), dtype=torch.float32, device=dev), Ci, Co)
+           for _ in range(n)]
     out = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
     out2 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
     ws = torch.empty((T, Co), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
 
     stages = ["quant_weight", "quant_act", "gemm_fused", "gemm_unfused"]
     run = set(args.only.split(",")) if args.only else set(stages)
@@ -461,107 +649,50 @@ def main():
     if unknown:
         raise SystemExit(f"unknown stages {sorted(unknown)}")
 
-    def step(ev=None):
+    def step(k, ev=None):
+        s = k % n
+
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
         if "quant_weight" in run:
-            sg.quant_weight(w, out=pw)
+            sg.quant_weight(wts[s], out=pws[s])
         mark(1)
         if "quant_act" in run:
-            sg.quant_act(x, qx=qx, dx=dx)
+            sg.quant_act(xs[s], qx=qxs[s], dx=dxs[s])
         mark(2)
         if "gemm_fused" in run:
-            sg.gemm(qx, dx, pw, out=out)
+            sg.gemm(qxs[s], dxs[s], pws[s], out=out)
         mark(3)
         if "gemm_unfused" in run:
-            sg.gemm_unfused(qx, dx, pw, out=out2, workspace=ws)
+            sg.gemm_unfused(qxs[s], dxs[s], pws[s], out=out2, workspace=ws)
         mark(4)
 
     # inputs of the GEMMs exist even when their producers are not timed
-    sg.quant_weight(w, out=pw)
-    sg.quant_act(x, qx=qx, dx=dx)
+    for s in range(n):
+        sg.quant_weight(wts[s], out=pws[s])
+        sg.quant_act(xs[s], qx=qxs[s], dx=dxs[s])
     if args.copy_calibration_mb:
-        n = args.copy_calibration_mb << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        nb = args.copy_calibration_mb << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        step(k, events[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-
-    # The per-tensor comparator on the same inputs (not part of the step):
-    # dynamic per-tensor activation scale + static cast, and the GEMM with
-    # scalar scales; the weight is quantized per tensor once, outside.
-    pt = None
-    if not args.only:
-        sw_t = sg.tensor_scale(w)
-        pw_t = sg.quant_weight_static(w, sw_t)
-        sx_t = torch.empty((1,), dtype=torch.float32, device=dev)
-        qx_t = torch.empty_like(qx)
-        out_t = torch.empty_like(out)
-        ws16 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
-        pt_calls = [("tensor_scale", lambda: sg.tensor_scale(x, d=sx_t)),
-                    ("quant_act_static", lambda: sg.quant_act_static(x, sx_t, qx=qx_t)),
-                    ("gemm_tensor", lambda: sg.gemm_tensor(qx_t, sx_t, pw_t, out=out_t)),
-                    ("gemm_unfused_bf16", lambda: sg.gemm_unfused_bf16(qx, dx, pw, out=out_t,
-                                                                       workspace=ws16))]
-        for _ in range(3):
-            for _, fn in pt_calls:
-                fn()
-        pt_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(pt_calls) + 1)]
-                 for _ in range(args.steps)]
-        for k in range(args.steps):
-            for i, (_, fn) in enumerate(pt_calls):
-                pt_ev[k][i].record(stream)
-                fn()
-            pt_ev[k][len(pt_calls)].record(stream)
-        torch.cuda.synchronize()
-        pt = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in pt_ev]))
-              for i, (name, _) in enumerate(pt_calls)}
-        del sw_t, pw_t, sx_t, qx_t, out_t, ws16
-
-    # References for the activation quantizer's HBM rate next to the 8 TB/s
-    # peak: a plain device copy (torch copy_, 512 MiB read + 512 MiB written)
-    # and torch's own unscaled bf16 -> float8_e4m3fn cast of the same X, which
-    # has exactly quant_act's traffic (2 bytes read, 1 written per element).
-    def timed(fn, n=5):
-        fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        for _ in range(n):
-            fn()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) * 1e-3 / n
-    copy_gbs = cast_gbs = float("nan")
-    # quant_act timed the same way as those references: back-to-back
-    # launches between one event pair (the per-launch pairs inside the step
-    # also span each launch's own gap, several us against a 58 us kernel).
-    act_batch_ms = float("nan")
-    if "quant_act" in run:
-        act_batch_ms = timed(lambda: sg.quant_act(x, qx=qx, dx=dx), n=20) * 1e3
-    if not args.only:
-        cp_src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
-        cp_dst = torch.empty_like(cp_src)
-        copy_gbs = 2.0 * cp_src.numel() / timed(lambda: cp_dst.copy_(cp_src)) / 1e9
-        del cp_src, cp_dst
-        cast_dst = torch.empty((T, Ci), dtype=torch.float8_e4m3fn, device=dev)
-        cast_gbs = act_bytes_ref(T, Ci) / timed(lambda: cast_dst.copy_(x)) / 1e9
-        del cast_dst
 
     per_stage = {s: [] for s in stages}
     for ev in events:
@@ -570,10 +701,97 @@ def main():
     avg = {s: float(np.mean(v)) for s, v in per_stage.items()}
     med = {s: float(np.median(v)) for s, v in per_stage.items()}
 
+    # The activation quantizer as a stream: back-to-back launches between one
+    # event pair, rotating over the input copies (the per-launch pairs inside
+    # the step also span each launch's own gap).
+    act_ms = act_ms_eager = float("nan")
+    act_reps = max(20, 2 * n)
+    if "quant_act" in run:
+        def act(i):
+            sg.quant_act(xs[i % n], qx=qxs[i % n], dx=dxs[i % n])
+        act_ms_eager = sorted(batch_ms(act, act_reps, stream) for _ in range(5))[2]
+        act_ms = graph_ms(act, act_reps, stream)
+
+    # Comparison forms on the same inputs, in interleaved rounds: each round
+    # runs every form once, on the next input copy, each between its own
+    # event pair, so that all forms see the same clock; ratios are the median
+    # of the per-round ratios.
+    cmp = None
+    copy_gbs = cast_gbs = float("nan")
+    if not args.only:
+        pwts, sxs = [], []
+        for s in range(n):
+            sw_t = sg.tensor_scale(wts[s])
+            pwts.append(sg.quant_weight_static(wts[s], sw_t))
+            sxs.append(sg.tensor_scale(xs[s]))
+        qx_t = torch.empty_like(qxs[0])
+        sx_t = torch.empty((1,), dtype=torch.float32, device=dev)
+        ws16 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
+        forms = {
+            "gemm_fused": lambda s: sg.gemm(qxs[s], dxs[s], pws[s], out=out),
+            "gemm_unfused": lambda s: sg.gemm_unfused(qxs[s], dxs[s], pws[s], out=out2,
+                                                      workspace=ws),
+            "gemm_unfused_bf16": lambda s: sg.gemm_unfused_bf16(qxs[s], dxs[s], pws[s], out=out2,
+                                                                workspace=ws16),
+            "gemm_tensor": lambda s: sg.gemm_tensor(qxs[s], sxs[s], pwts[s], out=out2),
+            "quant_act": lambda s: sg.quant_act(xs[s], qx=qxs[s], dx=dxs[s]),
+            "act_per_tensor": lambda s: (sg.tensor_scale(xs[s], d=sx_t),
+                                         sg.quant_act_static(xs[s], sx_t, qx=qx_t)),
+        }
+        for r in range(3):
+            for fn in forms.values():
+                fn(r % n)
+        torch.cuda.synchronize()
+        rounds = max(args.steps, 2 * n)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(forms))]
+               for _ in range(rounds)]
+        for r in range(rounds):
+            for i, fn in enumerate(forms.values()):
+                evs[r][2 * i].record(stream)
+                fn(r % n)
+                evs[r][2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        t = {k: np.array([e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs])
+             for i, k in enumerate(forms)}
+
+        def ratio(a, b):
+            return round(float(np.median(t[a] / t[b])), 4)
+
+        cmp = {
+            "timing": (f"{rounds} interleaved rounds, every form once per round on the next of "
+                       f"{n} input copies, each between its own HIP event pair; medians"),
+            "ms_median": {k: round(float(np.median(v)), 4) for k, v in t.items()},
+            "fused_gemm_tflops": round(2.0 * T * Ci * Co / np.median(t["gemm_fused"]) / 1e9, 1),
+            "two_step_fp32_over_fused": ratio("gemm_unfused", "gemm_fused"),
+            "two_step_bf16_over_fused": ratio("gemm_unfused_bf16", "gemm_fused"),
+            "ptpc_over_per_tensor_gemm": ratio("gemm_fused", "gemm_tensor"),
+            "ptpc_over_per_tensor_act_quant": ratio("quant_act", "act_per_tensor"),
+        }
+        del pwts, sxs, qx_t, ws16
+
+        # HBM references: a plain device copy (512 MiB read + 512 MiB written
+        # per launch, larger than the cache on its own) and torch's unscaled
+        # bf16 -> float8 cast of the same X copies (quant_act's traffic).
+        cp_src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        cp_dst = torch.empty_like(cp_src)
+        cp_dst.copy_(cp_src)
+        copy_gbs = 2.0 * cp_src.numel() / (batch_ms(lambda i: cp_dst.copy_(cp_src), 5, stream)
+                                           * 1e-3) / 1e9
+        del cp_src, cp_dst
+        cast_dst = torch.empty((T, Ci), dtype=torch.float8_e4m3fn, device=dev)
+        cast_dst.copy_(xs[0])
+        cast_gbs = 3.0 * T * Ci / (batch_ms(lambda i: cast_dst.copy_(xs[i % n]),
+                                            max(10, 2 * n), stream) * 1e-3) / 1e9
+        del cast_dst
+
+    judged = None
+    if not args.only and not args.no_judged:
+        del xs, wts, qxs, dxs, pws, out, out2, ws
+        torch.cuda.empty_cache()
+        judged = judged_shapes(stream)
+
     gemm_flops = 2.0 * T * Ci * Co
-    act_bytes = 3.0 * T * Ci + 4.0 * T
     w_bytes = 3.0 * Ci * Co + 4.0 * Co
-    fused_min_bytes = T * Ci + Ci * Co + 2.0 * T * Co + 4.0 * (T + Co)
     ms_per_step = elapsed * 1e3 / args.steps
     n_gemms = ("gemm_fused" in run) + ("gemm_unfused" in run)
     value = n_gemms * gemm_flops / (ms_per_step * 1e-3) / 1e12
@@ -583,9 +801,8 @@ def main():
 
     fused_tflops = rate(gemm_flops, "gemm_fused", 1e12)
     unfused_tflops = rate(gemm_flops, "gemm_unfused", 1e12)
-    act_gbs = act_bytes / (act_batch_ms * 1e-3) / 1e9 if "quant_act" in run else float("nan")
+    act_gbs = act_bytes(T, Ci) / (act_ms * 1e-3) / 1e9 if "quant_act" in run else float("nan")
     w_gbs = rate(w_bytes, "quant_weight", 1e9)
-    traffic = measured_traffic(shape.name)
 
     result = {
         "metric": "ptpc_gemm TFLOP/s (% FP8 MFMA peak); quant_act GB/s (% HBM) on 1 MI355X",
@@ -605,24 +822,32 @@ def main():
             "x": f"bf16 [{T}x{Ci}]", "w": f"bf16 [{Ci}x{Co}]", "out": f"bf16 [{T}x{Co}]",
             "step": " + ".join(s for s in stages if s in run),
             "value_work": f"{n_gemms} GEMMs x 2*T*Ci*Co flops per step",
+            "input_copies": n,
+            "rotation": (f"step k uses input copy k mod {n} (X, W and their quantized forms at "
+                         "distinct addresses): more than 768 MiB of other inputs pass between "
+                         "two uses of a copy, three times the 256 MB memory-side cache"),
         },
         "roofline": {
-            "kernel": "ptpc_gemm (fused)",
+            "kernel": "ptpc_gemm (fused): " + str(sg.gemm_kernel(T, Ci, Co)),
             "bound": "mfma",
             "achieved": round(fused_tflops, 1),
             "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(fused_tflops / PEAK_FP8_TFLOPS, 4),
-            "traffic": traffic,
-            "algorithmic_min_bytes": fused_min_bytes,
+            "traffic": measured_traffic(shape.name, "gemm_fused"),
+            "algorithmic_min_bytes": gemm_min_bytes(T, Ci, Co),
             "avg_launch_ms": round(avg["gemm_fused"], 4),
         },
         "quant_act": {
+            "kernel": sg.quant_act_kernel(T, Ci),
             "bound": "hbm", "achieved": round(act_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(act_gbs / PEAK_HBM_GBS, 4), "avg_launch_ms": round(act_batch_ms, 4),
-            "timing": "20 back-to-back launches between one HIP event pair on the launch stream",
+            "frac": round(act_gbs / PEAK_HBM_GBS, 4), "avg_launch_ms": round(act_ms, 4),
+            "timing": (f"{act_reps} launches rotating over {n} copies of X, captured in a HIP "
+                       "graph, median of 5 replays between one HIP event pair each"),
+            "eager_batch_ms": round(act_ms_eager, 4),
             "in_step_avg_launch_ms": round(avg["quant_act"], 4),
-            "bytes_per_launch": act_bytes,
+            "bytes_per_launch": act_bytes(T, Ci),
+            "traffic": measured_traffic(shape.name, "quant_act"),
             "device_copy_gbs": round(copy_gbs, 1),
             "torch_cast_gbs": round(cast_gbs, 1),
             "frac_of_torch_cast": round(act_gbs / cast_gbs, 4),
@@ -631,26 +856,10 @@ def main():
         "stages_ms_median": {k: round(v, 4) for k, v in med.items()},
         "quant_weight_gbs": round(w_gbs, 1),
         "gemm_unfused_tflops": round(unfused_tflops, 1),
-        "fused_over_unfused": (round(avg["gemm_unfused"] / avg["gemm_fused"], 3)
-                               if {"gemm_fused", "gemm_unfused"} <= run else None),
+        "comparison": cmp,
+        "judged_shapes": judged,
         "cpu_baseline": None,
     }
-    if pt is not None:
-        result["two_step_bf16"] = {
-            "what": "two-step form with a bf16 intermediate (GEMM -> bf16, then scale)",
-            "ms_avg": round(pt.pop("gemm_unfused_bf16"), 4),
-        }
-        result["two_step_bf16"]["fused_speedup"] = round(
-            result["two_step_bf16"]["ms_avg"] / avg["gemm_fused"], 4)
-        result["per_tensor"] = {
-            "what": "per-tensor FP8 comparator on the same inputs: tensor_scale(X) + "
-                    "quant_act_static + gemm_tensor (weight quantized per tensor once)",
-            "ms_avg": {k: round(v, 4) for k, v in pt.items()},
-            "gemm_tensor_tflops": round(gemm_flops / (pt["gemm_tensor"] * 1e-3) / 1e12, 1),
-            "ptpc_over_per_tensor_gemm_time": round(avg["gemm_fused"] / pt["gemm_tensor"], 4),
-            "ptpc_over_per_tensor_act_quant_time": round(
-                avg["quant_act"] / (pt["tensor_scale"] + pt["quant_act_static"]), 4),
-        }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, args.cpu_seconds)
     print(json.dumps(no_nan(result)), flush=True)

@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libptpc.so")
+# Debug variant: every pipelined GEMM kernel overwrites each LDS region it is
+# about to refill with E4M3 NaN bytes first (tests compare it with LIB).
+POISON_LIB = os.path.join(PKG, "libptpc_lds_poison.so")
 
 SOURCES = ["ptpc_api.cpp", "plan.cpp", "quant.hip", "gemm.hip"]
 
@@ -39,23 +42,33 @@ def _run(cmd, verbose):
     return r.stdout
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    objs = []
-    cmds = []
+def _variant(name, defines):
+    """(objects, compile commands, link command) of one build variant."""
+    out_dir = os.path.join(BUILD, name)
+    os.makedirs(out_dir, exist_ok=True)
+    lib = LIB if name == "release" else POISON_LIB
+    objs, cmds = [], []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
+        obj = os.path.join(out_dir, src.replace(".", "_") + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src),
-                     "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *defines, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
-    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-Bsymbolic",
+            "-o", lib + ".tmp", *objs]
+    return lib, cmds, link
+
+
+def build(verbose: bool = False) -> str:
+    """Build libptpc.so and its LDS-poison debug variant."""
+    variants = [_variant("release", []), _variant("lds_poison", ["-DPTPC_LDS_POISON"])]
+    cmds = [c for _, cs, _ in variants for c in cs]
+    with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for out in ex.map(lambda c: _run(c, verbose), cmds):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
+    for lib, _, link in variants:
+        _run(link, verbose)
+        os.replace(lib + ".tmp", lib)
     return LIB
 
 

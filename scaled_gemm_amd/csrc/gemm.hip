@@ -89,6 +89,25 @@ __device__ __forceinline__ void wait_counts() {
 
 constexpr int gcd_c(int a, int b) { return b == 0 ? a : gcd_c(b, a % b); }
 
+// LDS-poison debug build (-DPTPC_LDS_POISON, libptpc_lds_poison.so): right
+// before a wave issues the fills that refill an LDS region, it overwrites the
+// region with 0x7F bytes -- NaN as E4M3 -- and waits for those writes.  The
+// pipelines below issue a fill only once every wave's last read of the region
+// is done (behind a barrier, or the wave's own wait where a wave owns its
+// slots); a read that came too late, or one that came before its fill
+// landed, would now see NaN and turn the outputs it feeds into NaN, whatever
+// the data.  The parity tests compare the two builds bit for bit.
+#ifdef PTPC_LDS_POISON
+constexpr bool kLdsPoison = true;
+#else
+constexpr bool kLdsPoison = false;
+#endif
+__device__ __forceinline__ void poison_block(uint8_t* blk) {
+    const uint32_t nan4 = 0x7F7F7F7Fu;
+    *reinterpret_cast<uint4*>(blk + (threadIdx.x & 63) * 16) = make_uint4(nan4, nan4, nan4, nan4);
+}
+__device__ __forceinline__ void poison_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // Tile order.  Workgroups are dealt round-robin to the 8 XCDs, each with its
 // own L2.  The linear id is remapped so that XCD x owns a contiguous chunk of
 // the logical order, and the logical order walks groups of kGroupN column
@@ -331,6 +350,18 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
         constexpr int n = u + 1;
         const uint8_t* na = a_slots[(n / 2) % 3];
         const uint8_t* nb = b_slots[n % NB];
+        if constexpr (kLdsPoison) {
+            // the regions this step refills: B slot u % NB and one half of an
+            // A pair slot (see the fills below)
+#pragma unroll
+            for (int p = 0; p < B_PER_W; ++p) poison_block(b_slots[u % NB] + (wave + p * NW) * 1024);
+            constexpr int h = (u & 1) ? 0 : 1;
+            uint8_t* const as = a_slots[(u & 1) ? ((u + 5) / 2) % 3 : ((u + 4) / 2) % 3];
+#pragma unroll
+            for (int p = 0; p < A_HALF_PER_W; ++p)
+                poison_block(as + (h * (A_BLK / 2) + wave + p * NW) * 1024);
+            poison_done();
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < MT; ++i)
@@ -700,6 +731,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
         uint8_t* const fa = a_slot(u % 2);
         uint8_t* const fb = b_slot(u % 3);
         uint8_t* const fc = b_slot((u + 2) % 3);
+        if constexpr (kLdsPoison) {
+            // A slot u % 2 (A of step s, read during step s - 1) is refilled
+            // with A of step s + 2 from here on
+#pragma unroll
+            for (int p = 0; p < A_PER_W; ++p) poison_block(fa + wave * 1024 + p * NW * 1024);
+            poison_done();
+        }
         [&]<int... Js>(std::integer_sequence<int, Js...>) __attribute__((always_inline)) {
             ([&]() __attribute__((always_inline)) {
                 constexpr int j = Js;
@@ -718,7 +756,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
                 // Late slabs (from mid): the first B1 loads of B of step s+3.
                 constexpr int pb0 = j < NE ? 0 : (j - NE) * B1 / 2;
                 constexpr int pb1 = j < NE ? 0 : (j - NE + 1) * B1 / 2;
-                if constexpr (j == NE) sync(std::integral_constant<int, A_PER_W + B_PER_W>{});
+                if constexpr (j == NE) {
+                    sync(std::integral_constant<int, A_PER_W + B_PER_W>{});
+                    if constexpr (kLdsPoison) {
+                        // B slot u % 3 (B of step s, read up to here) takes
+                        // B of step s + 3 from here on, in both its parts
+#pragma unroll
+                        for (int p = 0; p < B_PER_W; ++p)
+                            poison_block(fb + wave * 1024 + p * NW * 1024);
+                        poison_done();
+                    }
+                }
                 // Side work of the slab in issue order: the A fragments and
                 // the B fragment first, then the fills.
                 constexpr int NIA = ia1 - ia0, NPA = pa1 - pa0, NPC = pc1 - pc0, NPB = pb1 - pb0;
@@ -1025,6 +1073,13 @@ __global__ __launch_bounds__(256, 1) void gemm16s_kernel(
         const uint8_t* const nb = b_slot((u + 1) % 3);
         uint8_t* const fa = a_slot(u % 2);
         uint8_t* const fb = b_slot(u % 3);
+        if constexpr (kLdsPoison) {
+            // this wave's A slot u % 2 (read during its previous step) takes
+            // A of its step i + 2 from here on
+#pragma unroll
+            for (int p = 0; p < NA; ++p) poison_block(fa + p * 1024);
+            poison_done();
+        }
         [&]<int... Js>(std::integer_sequence<int, Js...>) __attribute__((always_inline)) {
             ([&]() __attribute__((always_inline)) {
                 constexpr int j = Js;
@@ -1034,7 +1089,16 @@ __global__ __launch_bounds__(256, 1) void gemm16s_kernel(
                 constexpr int pa1 = j < NE ? (j + 1) * NA / NE : 0;
                 constexpr int pb0 = j < NE ? 0 : (j - NE) * NB / 2;
                 constexpr int pb1 = j < NE ? 0 : (j - NE + 1) * NB / 2;
-                if constexpr (j == NE) wait_counts<NA + NB, 0>();
+                if constexpr (j == NE) {
+                    wait_counts<NA + NB, 0>();
+                    if constexpr (kLdsPoison) {
+                        // this wave's B slot u % 3 (read up to here) takes B
+                        // of its step i + 3 from here on
+#pragma unroll
+                        for (int p = 0; p < NB; ++p) poison_block(fb + p * 1024);
+                        poison_done();
+                    }
+                }
                 constexpr int NPA = pa1 - pa0, NPB = pb1 - pb0;
                 constexpr int NITEM = 1 + 1 + NPA + NPB;
                 auto side = [&](auto Q) __attribute__((always_inline)) {

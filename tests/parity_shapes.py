@@ -53,7 +53,7 @@ TILE_CASES = [
     (1536, 592, 8192),      # 192x256 tiles, 5 K steps
     (1024, 880, 10240),     # 256x160 tiles, 7 K steps
     (1024, 752, 14336),     # 256x224 tiles, 6 K steps
-    (512, 16400, 1024),     # 128x256 tiles (long K), 129 K steps
+    (512, 16400, 1024),     # 128x128 tiles, long K: 129 K steps
     (512, 1040, 4096),      # 128x128 tiles at 256+ tokens, 9 K steps
     (256, 131072 - 16, 512),  # K near the contract's 2^17 limit, 128x128 tiles, 1024 K steps
 ]

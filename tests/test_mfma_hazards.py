@@ -131,16 +131,37 @@ def test_checker_catches_planted_hazards():
     assert _violations(skip, {".LBB0_2": 5})
 
 
-@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-def test_gemm16_inline_mfma_hazards(tmp_path):
-    out = tmp_path / "gemm.s"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++20", "-ffp-contract=off",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "scaled_gemm_amd", "csrc"),
-           "--cuda-device-only", "-S", "-x", "hip",
-           os.path.join(ROOT, "scaled_gemm_amd", "csrc", "gemm.hip"), "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True, timeout=600)
-    asm = out.read_text()
+VARIANTS = {"release": [], "lds_poison": ["-DPTPC_LDS_POISON"]}
+
+
+@pytest.fixture(scope="module")
+def gemm_asm(tmp_path_factory):
+    """gfx950 assembly of gemm.hip for the release and LDS-poison builds
+    (compiled once, in parallel)."""
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    d = tmp_path_factory.mktemp("asm")
+
+    def compile_one(item):
+        name, defines = item
+        out = d / f"gemm_{name}.s"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++20", "-ffp-contract=off",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *defines,
+               "-I", os.path.join(ROOT, "include"),
+               "-I", os.path.join(ROOT, "scaled_gemm_amd", "csrc"),
+               "--cuda-device-only", "-S", "-x", "hip",
+               os.path.join(ROOT, "scaled_gemm_amd", "csrc", "gemm.hip"), "-o", str(out)]
+        subprocess.run(cmd, check=True, capture_output=True, timeout=600)
+        return name, out.read_text()
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=2) as ex:
+        return dict(ex.map(compile_one, VARIANTS.items()))
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_gemm16_inline_mfma_hazards(gemm_asm, variant):
+    asm = gemm_asm[variant]
     found = 0
     for name, ins, labels in _functions(asm):
         found += 1
@@ -149,3 +170,25 @@ def test_gemm16_inline_mfma_hazards(tmp_path):
         bad = _violations(ins, labels)
         assert not bad, (name, bad[:5])
     assert found >= 10, "expected the fused and two-step forms of five kernels"
+
+
+def test_lds_poison_build_writes_its_poison(gemm_asm):
+    """The debug build really adds the poisoning LDS writes (16-byte writes
+    of 0x7F7F7F7F) to every pipelined kernel: more ds_write_b128 than the
+    release build in each of them, and the NaN pattern in the code."""
+    def writes(asm):
+        counts = {}
+        for m in re.finditer(r"\n(_ZN4ptpc(?:11gemm_kernel|13gemm16_kernel|14gemm16s_kernel)\w+):",
+                             asm):
+            body = asm[m.start():asm.index(".Lfunc_end", m.start())]
+            counts[m.group(1)] = sum(1 for line in body.split("\n")
+                                     if line.strip().startswith("ds_write_b128"))
+        return counts
+    rel = writes(gemm_asm["release"])
+    poi_asm = gemm_asm["lds_poison"]
+    poi = writes(poi_asm)
+    assert "0x7f7f7f7f" in poi_asm.lower()
+    piped = list(rel)
+    assert len(piped) >= 18          # fused and two-step forms of every tiled kernel
+    for n in piped:
+        assert poi[n] > rel[n], (n, rel[n], poi[n])

@@ -31,6 +31,14 @@ scaled in float32, then rounded to bf16 with round-to-nearest-even):
                 to a value drawn from U[500, 5e4] (sign drawn); for T = 1 the
                 single row gets that planted entry.  W ~ N(0, 0.01^2) per layer.
 
+  GPU draws     (timing only, no oracle side: the benchmark's per-shape
+                lines for the 70B layers at 1024 / 8192 tokens and the 8B
+                gate_up layer) the same value structure drawn on the GPU by
+                torch's seeded Philox generator: Student-t(3) as z / sqrt(chi2_3 / 3)
+                from four normals, times exp(1.5 n_k) per channel, one zero row
+                and one planted value in [500, 5e4]; or N(0,1) with 1% outlier
+                channels times U[20,100]; weights N(0, sigma^2).
+
   70b model load  (timing only, no oracle side) every linear weight of the
                 80 decoder layers, qkv / o / gate_up / down shapes as above,
                 W ~ N(0, 0.01^2) drawn in bf16 on the GPU by torch's seeded
@@ -195,3 +203,36 @@ def device_weight(layer: int, index: int, Ci: int, Co: int, sigma: float, device
     g.manual_seed(1000 * layer + index)
     return torch.empty((Ci, Co), device=device, dtype=torch.bfloat16).normal_(0.0, sigma,
                                                                              generator=g)
+
+
+def device_activation(kind: str, T: int, Ci: int, seed: int, device):
+    """Synthetic bf16 activations [T x Ci] drawn on `device` (timing only):
+    kind "student_lognormal" (the 70B layer sweep's structure) or
+    "outlier_normal" (the 8B layers' structure)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    f32 = dict(device=device, dtype=torch.float32)
+    if kind == "student_lognormal":
+        m = torch.exp(1.5 * torch.randn(Ci, generator=g, **f32))
+        x = torch.empty((T, Ci), device=device, dtype=torch.bfloat16)
+        step = max(1, (1 << 24) // Ci)
+        for r0 in range(0, T, step):
+            r1 = min(T, r0 + step)
+            z = torch.randn((r1 - r0, Ci), generator=g, **f32)
+            chi2 = torch.zeros_like(z)
+            for _ in range(3):
+                chi2.add_(torch.randn((r1 - r0, Ci), generator=g, **f32).square_())
+            x[r0:r1] = (z / torch.sqrt(chi2 / 3.0) * m).to(torch.bfloat16)
+        if T >= 16:
+            x[T // 3] = 0
+        x[T // 2, Ci // 5] = 12345.0
+        return x
+    if kind == "outlier_normal":
+        x = torch.randn((T, Ci), generator=g, **f32)
+        n_out = max(1, int(round(0.01 * Ci)))
+        ch = torch.randperm(Ci, generator=g, device=device)[:n_out]
+        fac = 20.0 + 80.0 * torch.rand(n_out, generator=g, **f32)
+        x[:, ch] *= fac
+        return x.to(torch.bfloat16)
+    raise KeyError(kind)
