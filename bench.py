@@ -554,13 +554,15 @@ def judged_shapes(stream, only=None):
             act(i)
         reps_g = max(2 * n, 10)
         reps_a = max(2 * nx, 20)
-        g_ms = sorted(batch_ms(gemm, reps_g, stream) for _ in range(5))[2]
+        g_eager = sorted(batch_ms(gemm, reps_g, stream) for _ in range(5))[2]
+        g_ms = graph_ms(gemm, reps_g, stream)
         a_ms = graph_ms(act, reps_a, stream)
         flops = 2.0 * T * Ci * Co
         res.append({
             "shape": f"{name}_T{T}", "T": T, "Ci": Ci, "Co": Co,
             "gemm_kernel": sg.gemm_kernel(T, Ci, Co),
-            "gemm_ms": round(g_ms, 4), "gemm_tflops": round(flops / g_ms / 1e9, 1),
+            "gemm_ms": round(g_ms, 4), "gemm_eager_batch_ms": round(g_eager, 4),
+            "gemm_tflops": round(flops / g_ms / 1e9, 1),
             "gemm_frac_fp8_peak": round(flops / g_ms / 1e9 / PEAK_FP8_TFLOPS, 4),
             "quant_act_ms": round(a_ms, 4),
             "quant_act_gbs": round(act_bytes(T, Ci) / a_ms / 1e6, 1),

@@ -6,14 +6,17 @@
 
 namespace ptpc {
 
-// Measured time of one tile relative to a 256x256 tile at the same K, on
-// the 8B / 70B layers (256x224, 192x256 and 256x128 on the 32x32x64 kernel,
-// 256x160 and 128x128 on the 16x16x128 one).
-constexpr double kCost256x128 = 0.69;
-constexpr double kCost256x224 = 0.92;
-constexpr double kCost128x128 = 0.55;
-constexpr double kCost256x160 = 0.83;
-constexpr double kCost192x256 = 0.88;
+// Time of one tile relative to a 256x256 tile at the same K, measured with
+// every operand streamed from HBM (inputs rotated over copies larger than the
+// memory-side cache, as a layer's weight arrives in a model's forward pass):
+// one round of tiles of each shape on the 70B O, down and QKV layers at 1024
+// tokens (the three layers agree within 0.02), and 128x128 per round on the
+// same layers' two- and three-round grids.
+constexpr double kCost256x224 = 0.94;
+constexpr double kCost192x256 = 0.85;
+constexpr double kCost256x160 = 0.90;
+constexpr double kCost128x256 = 0.75;    // 256x128 tiles, the same count, cost 0.88
+constexpr double kCost128x128 = 0.42;
 
 // 65..128 tokens where the tile rule below picks 64x64 tiles: those run
 // gemm16s_kernel (K split inside the workgroup), which needs no workspace
@@ -30,31 +33,36 @@ GemmPlan gemm_plan(int64_t T, int64_t Ci, int64_t Co) {
     auto rounds = [](int64_t tiles) { return (tiles + kCus - 1) / kCus; };
     auto tiles = [&](int64_t bm, int64_t bn) { return ((T + bm - 1) / bm) * ((Co + bn - 1) / bn); };
     if (T >= 256) {
-        // 256x256 keeps the most MFMA work per loaded byte; when it leaves
-        // CUs idle or a badly filled last round, 256x224 (4 waves side by
-        // side along the tokens), 192x256, 256x160, 256x128 or 128x128 -- more
-        // tiles, each cheaper -- is taken if its rounds of 256 CUs cost less
-        // (256x160: the 70B QKV layer at 1024 tokens, 256 tiles for 256 CUs,
-        // 6% faster than 192x256; 128x128: 256..600 tokens of the 8192-column
-        // layers, where 256-row tiles leave CUs idle, 18-29% faster).  Costs
-        // are in 256x256 tile-times: rounds times the relative tile cost.
-        const double c256 = (double)rounds(tiles(256, 256));
-        const double c128 = kCost256x128 * (double)rounds(tiles(256, 128));
-        const double c192 = kCost192x256 * (double)rounds(tiles(192, 256));
-        const double c224 = kCost256x224 * (double)rounds(tiles(256, 224));
-        const double c160 = kCost256x160 * (double)rounds(tiles(256, 160));
-        const double c1616 = kCost128x128 * (double)rounds(tiles(128, 128));
-        if (c1616 < c256 && c1616 < c128 && c1616 < c192 && c1616 < c160 && c1616 < c224)
-            return GemmPlan::k16_128x128;
-        if (c160 < c256 && c160 < c192 && c160 < c128 && c160 < c224) return GemmPlan::k16_256x160;
-        if (c224 < c256 && c224 < c192 && c224 < c128) return GemmPlan::k16_256x224;
-        // Long K: the same tile count as 256x128 tiles, whose eight column
-        // slabs per wave spread the fills more evenly (70B down projection at
-        // 1024 tokens: 6% faster; at K = 8192 the 256x128 form was 3-5% faster).
-        if (c128 < c256 && c128 <= c192 && Ci >= 16384) return GemmPlan::k16_128x256;
-        if (c128 < c256 && c128 <= c192) return GemmPlan::k16_256x128;
-        if (c192 < c256) return GemmPlan::k16_192x256;
-        return GemmPlan::k16_256x256;
+        // Each tile shape costs (rounds of 256 CUs it needs) x (its tile
+        // cost); the cheapest wins, the larger tile on a tie.  256x256 keeps
+        // the most MFMA work per loaded byte; the smaller tiles pay off where
+        // 256x256 tiles leave CUs idle or a badly filled last round (70B QKV
+        // at 1024 tokens: 240 tiles of 192x256 for 160 of 256x256; O and down:
+        // 256 tiles of 128x256; gate_up: 1024 of 256x224 for 3.5 rounds of
+        // 256x256; 256..600 tokens of the 8192-column layers: 128x128).
+        struct Cand {
+            GemmPlan plan;
+            int64_t bm, bn;
+            double cost;
+        };
+        const Cand cands[] = {
+            {GemmPlan::k16_256x256, 256, 256, 1.0},
+            {GemmPlan::k16_256x224, 256, 224, kCost256x224},
+            {GemmPlan::k16_192x256, 192, 256, kCost192x256},
+            {GemmPlan::k16_256x160, 256, 160, kCost256x160},
+            {GemmPlan::k16_128x256, 128, 256, kCost128x256},
+            {GemmPlan::k16_128x128, 128, 128, kCost128x128},
+        };
+        GemmPlan best = GemmPlan::k16_256x256;
+        double best_cost = 1e300;
+        for (const Cand& c : cands) {
+            const double cost = c.cost * (double)rounds(tiles(c.bm, c.bn));
+            if (cost < best_cost) {
+                best_cost = cost;
+                best = c.plan;
+            }
+        }
+        return best;
     }
     if (T > 64) {
         // 65..255 tokens: the fewest rounds of 256 CUs, and among equal
@@ -95,7 +103,6 @@ const char* gemm_plan_name(GemmPlan p) {
         case GemmPlan::k16_256x224: return "gemm16_kernel<256,224,4,1>";
         case GemmPlan::k16_256x160: return "gemm16_kernel<256,160,2,2>";
         case GemmPlan::k16_128x256: return "gemm16_kernel<128,256,2,2>";
-        case GemmPlan::k16_256x128: return "gemm16_kernel<256,128,2,2>";
         case GemmPlan::k16_128x128: return "gemm16_kernel<128,128,2,2>";
         case GemmPlan::k16s_64x64: return "gemm16s_kernel";
         case GemmPlan::k32_64x64: return "gemm_kernel<64,64,2,2,4>";

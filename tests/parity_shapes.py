@@ -51,7 +51,8 @@ FULL_SEEDS = [("tiny", 1), ("tiny", 2), ("8b_qkv_decode", 1), ("8b_qkv_decode", 
 TILE_CASES = [
     (4096, 1648, 4096),     # 256x256 tiles, 13 K steps
     (1536, 592, 8192),      # 192x256 tiles, 5 K steps
-    (1024, 880, 10240),     # 256x160 tiles, 7 K steps
+    (1024, 880, 10240),     # 192x256 tiles with a partial last row tile, 7 K steps
+    (256, 1040, 40944),     # 256x160 tiles with a partial last column tile, 9 K steps
     (1024, 752, 14336),     # 256x224 tiles, 6 K steps
     (512, 16400, 1024),     # 128x128 tiles, long K: 129 K steps
     (512, 1040, 4096),      # 128x128 tiles at 256+ tokens, 9 K steps

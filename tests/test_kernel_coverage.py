@@ -13,7 +13,7 @@ import parity_shapes
 # Every kernel the choice can return (one entry per instantiation).
 GEMM_KERNELS = {
     "gemm16_kernel<256,256,2,2>", "gemm16_kernel<192,256,2,2>", "gemm16_kernel<256,224,4,1>",
-    "gemm16_kernel<256,160,2,2>", "gemm16_kernel<128,256,2,2>", "gemm16_kernel<256,128,2,2>",
+    "gemm16_kernel<256,160,2,2>", "gemm16_kernel<128,256,2,2>",
     "gemm16_kernel<128,128,2,2>", "gemm16s_kernel", "gemm_kernel<64,64,2,2,4>",
     "gemm_kernel<64,128,2,2,4>", "gemm_kernel<128,128,2,2,4>", "gemm_kernel<32,64,1,2,4>",
     "gemm_decode_kernel<2,2,4,4>", "gemm_decode_kernel<2,1,4,4>",
