@@ -85,6 +85,9 @@ def parse(argv=None):
                         "--only <kernel> --copy-calibration-mb run into the traffic record of "
                         "--traffic-kernel and exit (no GPU needed)")
     p.add_argument("--traffic-kernel", default="gemm_fused", choices=sorted(TRAFFIC))
+    p.add_argument("--timeline", action="store_true",
+                   help="per-workgroup phases of the tiled GEMM (timeline debug build) on the "
+                        "bench workload and the judged shapes; one JSON line per shape")
     return p.parse_args(argv)
 
 
@@ -141,6 +144,12 @@ def traffic_record(fetch_csv, write_csv, workload, copy_mb, kind):
                 key = "kernel" if match in name else "copy" if "copyBuffer" in name else None
                 if key:
                     vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        # The input copies of the rotation are device copies too; the
+        # calibration copies are the largest of the run (copy_mb, more than
+        # any input copy): keep only those.
+        big = max(vals["copy"])
+        vals["copy"] = [v for v in vals["copy"] if v >= 0.95 * big]
+        assert len(vals["copy"]) == 3, "expected the three calibration copies"
         return {k: sum(v) / len(v) for k, v in vals.items()}
 
     f = per_kernel(fetch_csv, "FETCH_SIZE")
@@ -577,6 +586,121 @@ def judged_shapes(stream, only=None):
 
 
 # ---------------------------------------------------------------------------
+# timeline of the tiled GEMM (debug build)
+# ---------------------------------------------------------------------------
+def timeline(args):
+    """Where the fused GEMM's time goes, per workgroup: the timeline debug
+    build of the library (libptpc_timeline.so) records, for every workgroup
+    of the tiled kernel, its start, the moment its K loop begins (first
+    operands landed), the end of its K loop and the completion of its last
+    output store.  Inputs are drawn on the GPU (the 70B layers' Student-t x
+    log-normal structure, the 8B layers' outlier channels) and rotate over
+    copies as in every other timing; after
+    a warm-up of back-to-back launches, three launches are recorded, each
+    between its own HIP event pair; the median one is reported.  Workgroups
+    are grouped into rounds of 256 (one per CU) by start time."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import scaled_gemm_amd as sg
+    import workloads
+    from scaled_gemm_amd import build
+
+    dev = torch.device("cuda:0")
+    sg.lib()
+    stream = torch.cuda.current_stream()
+    L = ctypes.CDLL(build.TIMELINE_LIB)
+    P, I = ctypes.c_void_p, ctypes.c_int64
+    L.ptpc_gemm.restype = ctypes.c_int
+    L.ptpc_gemm.argtypes = [P, I, P, P, P, I, I, I, P, I, P]
+    L.ptpc_debug_set_timeline.restype = ctypes.c_int
+    L.ptpc_debug_set_timeline.argtypes = [P]
+    shapes = [("70b_down", 4096, 28672, 8192, "student_lognormal", 0.01),
+              ("8b_gate_up", 2048, 4096, 28672, "outlier_normal", 0.02)]
+    shapes += [(f"70b_{layer}", T, Ci, Co, "student_lognormal", 0.01)
+               for layer, (Ci, Co) in workloads.SWEEP_LAYERS.items() for T in (1024, 8192)]
+    for k, (name, T, Ci, Co, kind, sigma) in enumerate(shapes):
+        kname = sg.gemm_kernel(T, Ci, Co)
+        if not kname.startswith("gemm16_kernel<"):
+            continue
+        bm, bn = (int(v) for v in kname[len("gemm16_kernel<"):].split(",")[:2])
+        x = workloads.device_activation(kind, T, Ci, 9000 + k, dev)
+        w = workloads.device_weight(200, k, Ci, Co, sigma, dev)
+        pw = sg.quant_weight(w)
+        del w
+        qx, dx = sg.quant_act(x)
+        del x
+        n = n_sets(T * Ci + pw.data.numel())
+        pws = [pw] + [sg.PackedWeight(pw.data.clone(), pw.dw.clone(), Ci, Co) for _ in range(n - 1)]
+        qxs = [qx] + [qx.clone() for _ in range(n - 1)]
+        out = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
+        ref = sg.gemm(qx, dx, pw)
+        wgs = ((T + bm - 1) // bm) * ((Co + bn - 1) // bn)
+        buf = torch.zeros((wgs, 4), dtype=torch.int64, device=dev)
+
+        def run(i):
+            assert L.ptpc_gemm(P(qxs[i % n].data_ptr()), Ci, P(dx.data_ptr()),
+                               P(pws[i % n].data.data_ptr()), P(pws[i % n].dw.data_ptr()), T, Ci,
+                               Co, P(out.data_ptr()), Co, P(stream.cuda_stream)) == 0
+
+        assert L.ptpc_debug_set_timeline(None) == 0
+        for i in range(2 * n):
+            run(i)
+        torch.cuda.synchronize()
+        same = torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        recs = []
+        for rep in range(3):
+            buf.zero_()
+            torch.cuda.synchronize()
+            assert L.ptpc_debug_set_timeline(P(buf.data_ptr())) == 0
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run(rep + 1)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            assert L.ptpc_debug_set_timeline(None) == 0
+            t = buf.cpu().numpy().astype(np.float64) * 0.01          # 100 MHz ticks -> us
+            assert np.all(t[:, 0] > 0), "a workgroup did not record"
+            t -= t[:, 0].min()
+            recs.append((e0.elapsed_time(e1) * 1e3, t))
+        recs.sort(key=lambda r: r[0])
+        ev_us, t = recs[1]
+        pro, kl, epi = t[:, 1] - t[:, 0], t[:, 2] - t[:, 1], t[:, 3] - t[:, 2]
+        order = np.argsort(t[:, 0])
+        rounds = []
+        for r0 in range(0, wgs, 256):
+            idx = order[r0:r0 + 256]
+            rounds.append({"workgroups": int(idx.size),
+                           "start_us": [round(float(t[idx, 0].min()), 2),
+                                        round(float(t[idx, 0].max()), 2)],
+                           "end_us": [round(float(t[idx, 3].min()), 2),
+                                      round(float(t[idx, 3].max()), 2)],
+                           "prologue_us_median": round(float(np.median(pro[idx])), 2),
+                           "k_loop_us_median": round(float(np.median(kl[idx])), 2),
+                           "epilogue_us_median": round(float(np.median(epi[idx])), 2)})
+        tile_flops = 2.0 * bm * bn * round_k(Ci)
+        kl_rate = tile_flops / (np.median(kl) * 1e-6) * 256 / 1e12
+        flops = 2.0 * T * Ci * Co
+        print(json.dumps({
+            "shape": f"{name}_T{T}", "T": T, "Ci": Ci, "Co": Co, "kernel": kname,
+            "workgroups": wgs, "output_equals_release": same,
+            "event_us": round(ev_us, 2), "span_us": round(float(t[:, 3].max()), 2),
+            "frac_fp8_peak_event": round(flops / (ev_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "prologue_us": [round(float(v), 2) for v in np.percentile(pro, [10, 50, 90])],
+            "k_loop_us": [round(float(v), 2) for v in np.percentile(kl, [10, 50, 90])],
+            "epilogue_us": [round(float(v), 2) for v in np.percentile(epi, [10, 50, 90])],
+            "k_loop_tflops_if_256_cus": round(float(kl_rate), 1),
+            "k_loop_frac_fp8_peak": round(float(kl_rate) / PEAK_FP8_TFLOPS, 4),
+            "rounds": rounds,
+        }), flush=True)
+        del pws, qxs, out, ref, buf, pw, qx, dx
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
 # the bench line
 # ---------------------------------------------------------------------------
 def main():
@@ -594,6 +718,9 @@ def main():
         return
     if args.scaled_mm_context:
         scaled_mm_context(args)
+        return
+    if args.timeline:
+        timeline(args)
         return
     if args.traffic_from:
         rec = traffic_record(args.traffic_from[0], args.traffic_from[1], args.workload,
@@ -629,18 +756,21 @@ def main():
     x0 = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     w0 = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # Input copies at distinct addresses; step k works on copy k mod n, so
-    # every stage reads inputs no repetition touched for n - 1 steps (more
-    # than 768 MiB of other data in between).  Outputs are written, not read,
-    # and are shared.
-    n = n_sets(min(2 * T * Ci, T * Ci + Co * round_k(Ci)))
-    xs = [x0] + [x0.clone() for _ in range(n - 1)]
-    wts = [w0] + [w0.clone() for _ in range(n - 1)]
-    qxs = [torch.empty((T, Ci), dtype=torch.uint8, device=dev) for _ in range(n)]
-    dxs = [torch.empty((T,), dtype=torch.float32, device=dev) for _ in range(n)]
+    # Input copies at distinct addresses: step k works on activation copy
+    # k mod nx and weight copy k mod nw, each count sized so that more than
+    # 768 MiB of other copies pass between two uses of one (so every stage
+    # reads inputs from HBM, not from the memory-side cache).  Outputs are
+    # written, not read, and are shared.
+    nx = n_sets(2 * T * Ci)
+    nw = n_sets(Co * round_k(Ci))
+    n = max(nx, nw)
+    xs = [x0] + [x0.clone() for _ in range(nx - 1)]
+    wts = [w0] + [w0.clone() for _ in range(nw - 1)]
+    qxs = [torch.empty((T, Ci), dtype=torch.uint8, device=dev) for _ in range(nx)]
+    dxs = [torch.empty((T,), dtype=torch.float32, device=dev) for _ in range(nx)]
     pws = [sg.PackedWeight(torch.empty((sg.packed_bytes(Ci, Co),), dtype=torch.uint8, device=dev),
                            torch.empty((Co,), dtype=torch.float32, device=dev), Ci, Co)
-           for _ in range(n)]
+           for _ in range(nw)]
     out = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
     out2 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
     ws = torch.empty((T, Co), dtype=torch.float32, device=dev)
@@ -652,29 +782,30 @@ def main():
         raise SystemExit(f"unknown stages {sorted(unknown)}")
 
     def step(k, ev=None):
-        s = k % n
+        a, b = k % nx, k % nw
 
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
         if "quant_weight" in run:
-            sg.quant_weight(wts[s], out=pws[s])
+            sg.quant_weight(wts[b], out=pws[b])
         mark(1)
         if "quant_act" in run:
-            sg.quant_act(xs[s], qx=qxs[s], dx=dxs[s])
+            sg.quant_act(xs[a], qx=qxs[a], dx=dxs[a])
         mark(2)
         if "gemm_fused" in run:
-            sg.gemm(qxs[s], dxs[s], pws[s], out=out)
+            sg.gemm(qxs[a], dxs[a], pws[b], out=out)
         mark(3)
         if "gemm_unfused" in run:
-            sg.gemm_unfused(qxs[s], dxs[s], pws[s], out=out2, workspace=ws)
+            sg.gemm_unfused(qxs[a], dxs[a], pws[b], out=out2, workspace=ws)
         mark(4)
 
     # inputs of the GEMMs exist even when their producers are not timed
-    for s in range(n):
-        sg.quant_weight(wts[s], out=pws[s])
-        sg.quant_act(xs[s], qx=qxs[s], dx=dxs[s])
+    for b in range(nw):
+        sg.quant_weight(wts[b], out=pws[b])
+    for a in range(nx):
+        sg.quant_act(xs[a], qx=qxs[a], dx=dxs[a])
     if args.copy_calibration_mb:
         nb = args.copy_calibration_mb << 20
         src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
@@ -707,10 +838,10 @@ def main():
     # event pair, rotating over the input copies (the per-launch pairs inside
     # the step also span each launch's own gap).
     act_ms = act_ms_eager = float("nan")
-    act_reps = max(20, 2 * n)
+    act_reps = max(20, 2 * nx)
     if "quant_act" in run:
         def act(i):
-            sg.quant_act(xs[i % n], qx=qxs[i % n], dx=dxs[i % n])
+            sg.quant_act(xs[i % nx], qx=qxs[i % nx], dx=dxs[i % nx])
         act_ms_eager = sorted(batch_ms(act, act_reps, stream) for _ in range(5))[2]
         act_ms = graph_ms(act, act_reps, stream)
 
@@ -721,28 +852,27 @@ def main():
     cmp = None
     copy_gbs = cast_gbs = float("nan")
     if not args.only:
-        pwts, sxs = [], []
-        for s in range(n):
-            sw_t = sg.tensor_scale(wts[s])
-            pwts.append(sg.quant_weight_static(wts[s], sw_t))
-            sxs.append(sg.tensor_scale(xs[s]))
+        pwts = [sg.quant_weight_static(wts[b], sg.tensor_scale(wts[b])) for b in range(nw)]
+        sxs = [sg.tensor_scale(xs[a]) for a in range(nx)]
         qx_t = torch.empty_like(qxs[0])
         sx_t = torch.empty((1,), dtype=torch.float32, device=dev)
         ws16 = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
         forms = {
-            "gemm_fused": lambda s: sg.gemm(qxs[s], dxs[s], pws[s], out=out),
-            "gemm_unfused": lambda s: sg.gemm_unfused(qxs[s], dxs[s], pws[s], out=out2,
-                                                      workspace=ws),
-            "gemm_unfused_bf16": lambda s: sg.gemm_unfused_bf16(qxs[s], dxs[s], pws[s], out=out2,
+            "gemm_fused": lambda r: sg.gemm(qxs[r % nx], dxs[r % nx], pws[r % nw], out=out),
+            "gemm_unfused": lambda r: sg.gemm_unfused(qxs[r % nx], dxs[r % nx], pws[r % nw],
+                                                      out=out2, workspace=ws),
+            "gemm_unfused_bf16": lambda r: sg.gemm_unfused_bf16(qxs[r % nx], dxs[r % nx],
+                                                                pws[r % nw], out=out2,
                                                                 workspace=ws16),
-            "gemm_tensor": lambda s: sg.gemm_tensor(qxs[s], sxs[s], pwts[s], out=out2),
-            "quant_act": lambda s: sg.quant_act(xs[s], qx=qxs[s], dx=dxs[s]),
-            "act_per_tensor": lambda s: (sg.tensor_scale(xs[s], d=sx_t),
-                                         sg.quant_act_static(xs[s], sx_t, qx=qx_t)),
+            "gemm_tensor": lambda r: sg.gemm_tensor(qxs[r % nx], sxs[r % nx], pwts[r % nw],
+                                                    out=out2),
+            "quant_act": lambda r: sg.quant_act(xs[r % nx], qx=qxs[r % nx], dx=dxs[r % nx]),
+            "act_per_tensor": lambda r: (sg.tensor_scale(xs[r % nx], d=sx_t),
+                                         sg.quant_act_static(xs[r % nx], sx_t, qx=qx_t)),
         }
         for r in range(3):
             for fn in forms.values():
-                fn(r % n)
+                fn(r)
         torch.cuda.synchronize()
         rounds = max(args.steps, 2 * n)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(forms))]
@@ -750,7 +880,7 @@ def main():
         for r in range(rounds):
             for i, fn in enumerate(forms.values()):
                 evs[r][2 * i].record(stream)
-                fn(r % n)
+                fn(r)
                 evs[r][2 * i + 1].record(stream)
         torch.cuda.synchronize()
         t = {k: np.array([e[2 * i].elapsed_time(e[2 * i + 1]) for e in evs])
@@ -760,8 +890,9 @@ def main():
             return round(float(np.median(t[a] / t[b])), 4)
 
         cmp = {
-            "timing": (f"{rounds} interleaved rounds, every form once per round on the next of "
-                       f"{n} input copies, each between its own HIP event pair; medians"),
+            "timing": (f"{rounds} interleaved rounds, every form once per round on the next "
+                       f"input copies ({nx} of X, {nw} of W), each between its own HIP event "
+                       "pair; medians"),
             "ms_median": {k: round(float(np.median(v)), 4) for k, v in t.items()},
             "fused_gemm_tflops": round(2.0 * T * Ci * Co / np.median(t["gemm_fused"]) / 1e9, 1),
             "two_step_fp32_over_fused": ratio("gemm_unfused", "gemm_fused"),
@@ -782,8 +913,8 @@ def main():
         del cp_src, cp_dst
         cast_dst = torch.empty((T, Ci), dtype=torch.float8_e4m3fn, device=dev)
         cast_dst.copy_(xs[0])
-        cast_gbs = 3.0 * T * Ci / (batch_ms(lambda i: cast_dst.copy_(xs[i % n]),
-                                            max(10, 2 * n), stream) * 1e-3) / 1e9
+        cast_gbs = 3.0 * T * Ci / (batch_ms(lambda i: cast_dst.copy_(xs[i % nx]),
+                                            max(10, 2 * nx), stream) * 1e-3) / 1e9
         del cast_dst
 
     judged = None
@@ -824,10 +955,11 @@ def main():
             "x": f"bf16 [{T}x{Ci}]", "w": f"bf16 [{Ci}x{Co}]", "out": f"bf16 [{T}x{Co}]",
             "step": " + ".join(s for s in stages if s in run),
             "value_work": f"{n_gemms} GEMMs x 2*T*Ci*Co flops per step",
-            "input_copies": n,
-            "rotation": (f"step k uses input copy k mod {n} (X, W and their quantized forms at "
-                         "distinct addresses): more than 768 MiB of other inputs pass between "
-                         "two uses of a copy, three times the 256 MB memory-side cache"),
+            "input_copies": {"x": nx, "w": nw},
+            "rotation": (f"step k uses copy k mod {nx} of X (and its codes) and copy k mod {nw} "
+                         "of W (and its packed form), at distinct addresses: more than 768 MiB "
+                         "of other copies pass between two uses of one, three times the 256 MB "
+                         "memory-side cache"),
         },
         "roofline": {
             "kernel": "ptpc_gemm (fused): " + str(sg.gemm_kernel(T, Ci, Co)),
@@ -844,7 +976,7 @@ def main():
             "kernel": sg.quant_act_kernel(T, Ci),
             "bound": "hbm", "achieved": round(act_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(act_gbs / PEAK_HBM_GBS, 4), "avg_launch_ms": round(act_ms, 4),
-            "timing": (f"{act_reps} launches rotating over {n} copies of X, captured in a HIP "
+            "timing": (f"{act_reps} launches rotating over {nx} copies of X, captured in a HIP "
                        "graph, median of 5 replays between one HIP event pair each"),
             "eager_batch_ms": round(act_ms_eager, 4),
             "in_step_avg_launch_ms": round(avg["quant_act"], 4),

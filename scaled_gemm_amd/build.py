@@ -19,6 +19,10 @@ LIB = os.path.join(PKG, "libptpc.so")
 # Debug variant: every pipelined GEMM kernel overwrites each LDS region it is
 # about to refill with E4M3 NaN bytes first (tests compare it with LIB).
 POISON_LIB = os.path.join(PKG, "libptpc_lds_poison.so")
+# Debug variant: the main tiled GEMM kernel records per-workgroup timestamps
+# (start, K loop entered, K loop done, stores done) into a buffer set with
+# ptpc_debug_set_timeline (bench.py --timeline).
+TIMELINE_LIB = os.path.join(PKG, "libptpc_timeline.so")
 
 SOURCES = ["ptpc_api.cpp", "plan.cpp", "quant.hip", "gemm.hip"]
 
@@ -46,7 +50,7 @@ def _variant(name, defines):
     """(objects, compile commands, link command) of one build variant."""
     out_dir = os.path.join(BUILD, name)
     os.makedirs(out_dir, exist_ok=True)
-    lib = LIB if name == "release" else POISON_LIB
+    lib = {"release": LIB, "lds_poison": POISON_LIB, "timeline": TIMELINE_LIB}[name]
     objs, cmds = [], []
     for src in SOURCES:
         obj = os.path.join(out_dir, src.replace(".", "_") + ".o")
@@ -59,8 +63,9 @@ def _variant(name, defines):
 
 
 def build(verbose: bool = False) -> str:
-    """Build libptpc.so and its LDS-poison debug variant."""
-    variants = [_variant("release", []), _variant("lds_poison", ["-DPTPC_LDS_POISON"])]
+    """Build libptpc.so and its two debug variants."""
+    variants = [_variant("release", []), _variant("lds_poison", ["-DPTPC_LDS_POISON"]),
+                _variant("timeline", ["-DPTPC_TIMELINE"])]
     cmds = [c for _, cs, _ in variants for c in cs]
     with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for out in ex.map(lambda c: _run(c, verbose), cmds):

@@ -108,6 +108,24 @@ __device__ __forceinline__ void poison_block(uint8_t* blk) {
 }
 __device__ __forceinline__ void poison_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Timeline debug build (-DPTPC_TIMELINE, libptpc_timeline.so): wave 0 of
+// every workgroup of gemm16_kernel records the GPU's constant 100 MHz clock
+// (s_memrealtime) at four points -- start, K loop entered (first operands
+// landed), K loop done, last output store completed -- into the buffer set
+// with ptpc_debug_set_timeline ([workgroups][4] uint64, or NULL for none).
+#ifdef PTPC_TIMELINE
+__device__ unsigned long long* g_timeline = nullptr;
+#endif
+__device__ __forceinline__ void timeline_mark(int k) {
+#ifdef PTPC_TIMELINE
+    if (k == 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (threadIdx.x == 0 && g_timeline != nullptr)
+        g_timeline[(size_t)blockIdx.x * 4 + k] = __builtin_amdgcn_s_memrealtime();
+#else
+    (void)k;
+#endif
+}
+
 // Tile order.  Workgroups are dealt round-robin to the 8 XCDs, each with its
 // own L2.  The linear id is remapped so that XCD x owns a contiguous chunk of
 // the logical order, and the logical order walks groups of kGroupN column
@@ -619,6 +637,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
         return k == 0 ? b_s0 : k == 1 ? b_s1 : b_s2;
     };
 
+    timeline_mark(0);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -839,6 +858,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
         for (int p = 0; p < B1; ++p) issue_b(2, p, b_s2);
         __builtin_amdgcn_sched_barrier(0);
         sync(std::integral_constant<int, A_PER_W + B_PER_W + B1>{});   // A0, B0
+        timeline_mark(1);
 #pragma unroll
         for (int i = 0; i < MT; ++i) fr_a[0][i] = read_a(a_s0, i);
         fr_b[0] = read_b(b_s0, 0);
@@ -864,6 +884,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
         }(std::make_integer_sequence<int, P - 1>{});
         wait_counts<0, 0>();
         lds_barrier();
+        timeline_mark(2);
     }
 
     // Epilogue.  The weight slab is the MFMA's first operand, so the 16x16
@@ -946,6 +967,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
             }
         }
     }
+    timeline_mark(3);
 }
 
 // 65..128 tokens on 64x64 tiles: the 16x16x128 pipeline with the K steps dealt to the four
@@ -1658,6 +1680,12 @@ hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, c
 // needs clearing between calls; calls that overlap on one GPU share the
 // array and race.
 static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+#ifdef PTPC_TIMELINE
+extern "C" int ptpc_debug_set_timeline(void* buf) {
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_timeline), &buf, sizeof(buf));
+}
+#endif
 
 hipError_t noalloc_scratch(void** ptr) {
     constexpr int kMaxDevices = 64;

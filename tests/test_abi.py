@@ -216,3 +216,18 @@ def test_noalloc_scratch_covers_every_split(L):
     assert f(A, 256, B, C, D, 4, 256, 500, E, 512, None) == 3
     assert f(NULL, 256, B, C, D, 4, 256, 512, E, 512, None) == 1
     assert f(A, 256, B, C, D, 4, 256, 512, E, 516, None) == 4
+
+
+def test_debug_builds_export_the_abi():
+    """The two debug builds export every symbol of include/ptpc.h, and the
+    timeline build also the call of include/ptpc_debug.h."""
+    from scaled_gemm_amd import build
+    dbg = sorted(set(re.findall(r"\b(ptpc_[a-z0-9_]+)\s*\(",
+                                open(os.path.join(ROOT, "include", "ptpc_debug.h")).read())))
+    assert dbg == ["ptpc_debug_set_timeline"]
+    for lib, extra in ((build.POISON_LIB, []), (build.TIMELINE_LIB, dbg)):
+        out = subprocess.run(["nm", "-D", "--defined-only", lib], check=True,
+                             stdout=subprocess.PIPE, text=True).stdout
+        exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+        for name in declared_functions() + extra:
+            assert name in exported, (lib, name)
