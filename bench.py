@@ -423,10 +423,11 @@ def scaled_mm_context(args):
 
 def sweep(args):
     """Per-shape kernel rates over every workload shape.  After a warm-up,
-    three interleaved rounds over the stages, each round one HIP event pair
-    on the launch stream around back-to-back launches that rotate over
-    copies of the inputs (more than 768 MiB between two uses of a copy); the
-    best round per stage."""
+    three interleaved rounds over the stages; each round captures a run of
+    launches rotating over copies of the inputs (more than 768 MiB between
+    two uses of a copy) in a HIP graph and times its replays (median of 3,
+    each between one HIP event pair), so that the host's per-call cost does
+    not enter the few-microsecond shapes; the best round per stage."""
     import numpy as np
     import torch
 
@@ -488,7 +489,7 @@ def sweep(args):
         reps = max(args.steps, 2 * max(n, nx))
         for _ in range(3):
             for k, fn in calls.items():
-                rounds[k].append(batch_ms(fn, reps, stream))
+                rounds[k].append(graph_ms(fn, reps, stream, replays=3))
         ms = {k: min(v) for k, v in rounds.items()}
         flops = 2.0 * T * Ci * Co
         ab = act_bytes(T, Ci)
