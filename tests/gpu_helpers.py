@@ -1,4 +1,6 @@
 """Shared helpers for the GPU parity tests (host side only)."""
+import os
+
 import numpy as np
 import torch
 
@@ -43,9 +45,13 @@ def check_close(gpu_bits: np.ndarray, ref: np.ndarray, what: str):
     max_err = float(err.max()) if err.size else 0.0
     assert max_err <= MAX_REL * scale, f"{what}: max err {max_err} > 2^-7 * {scale}"
     nrm = float(np.linalg.norm(ref))
-    if nrm > 0:
-        rel = float(np.linalg.norm(got - ref)) / nrm
-        assert rel <= L2_REL, f"{what}: rel L2 {rel} > {L2_REL}"
+    rel = float(np.linalg.norm(got - ref)) / nrm if nrm > 0 else 0.0
+    log = os.environ.get("PTPC_PARITY_LOG")
+    if log:
+        # one line per checked output set: the figures the bar is applied to
+        with open(log, "a") as f:
+            f.write(f"{what}\t{got.size}\t{max_err / scale if scale else 0.0:.3e}\t{rel:.3e}\n")
+    assert rel <= L2_REL, f"{what}: rel L2 {rel} > {L2_REL}"
     return max_err, scale
 
 
