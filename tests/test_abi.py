@@ -136,6 +136,7 @@ def test_gemm_validation(L):
     assert L.ptpc_gemm_workspace_bytes(16, 8192, 8192) == 0             # few-token kernel
     assert L.ptpc_gemm_workspace_bytes(128, 8192, 57344) == 0           # 448 tiles
     assert L.ptpc_gemm_workspace_bytes(128, 8192, 8192) == 0            # K split in-workgroup
+    assert L.ptpc_gemm_workspace_bytes(128, 28672, 8192) == 4 * 4 * 128 * 8192  # long K: split
     g = L.ptpc_gemm_ws
     assert g(A, 8192, B, C, D, 128, 8192, 10240, E, 10240, NULL, 0, None) == 1
     assert g(A, 8192, B, C, D, 128, 8192, 10240, E, 10240, D, need - 16, None) == 2

@@ -414,14 +414,16 @@ def test_gemm_ws_split_k_ragged():
 
 def test_gemm_ws_sweep_t128():
     """The 70B layers at 128 tokens through ptpc_gemm_ws (QKV: 3 K ranges;
-    O and down, whose 64x64 tiles split K inside the workgroup, and gate_up:
-    no split -> bit-identical to ptpc_gemm)."""
+    down, K = 28672: 4; O, whose 64x64 tiles split K inside the workgroup,
+    and gate_up: no split -> bit-identical to ptpc_gemm)."""
     for layer in workloads.SWEEP_LAYERS:
         shape, x, w = workloads.make("70b_sweep", T=128, layer=layer)
         note(f"split-K 70b {layer} T=128")
         qx, dx = sg.quant_act(bits_to_dev(x))
         pw = sg.quant_weight(bits_to_dev(w))
-        out = dev_to_bits(sg.gemm_ws(qx, dx, pw))
+        o = sg.gemm_ws(qx, dx, pw, out=nan_filled(128, shape.Co))
+        no_nan(o, f"{shape.name} split-K")
+        out = dev_to_bits(o)
         plain = dev_to_bits(sg.gemm(qx, dx, pw))
         if sg.gemm_workspace_bytes(128, shape.Ci, shape.Co) == 0:
             assert np.array_equal(out, plain)
