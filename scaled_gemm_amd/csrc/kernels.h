@@ -12,6 +12,11 @@ namespace ptpc {
 // this many workgroups.
 constexpr int64_t kCus = 256;
 
+// "Long K" for the split-K choices (K = Ci bytes of FP8 per row): from here
+// on the workspace form splits the K-split 64x64 tile shapes too, and its
+// split kernel's weight fills carry the non-temporal hint.
+constexpr int64_t kLongK = 16384;
+
 // K extent of the packed weight: whole 128-byte K tiles.
 inline int64_t round_up_k(int64_t Ci) { return (Ci + 127) / 128 * 128; }
 

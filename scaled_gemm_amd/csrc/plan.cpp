@@ -125,9 +125,8 @@ const char* gemm_plan_name(GemmPlan p) {
 // operand bytes of 128x128 tiles into LDS, which outweighs the fp32 partials'
 // round trip once K is long (70B down projection, K = 28672, 72 / 128 tokens:
 // 19% / 28% faster; 70B O projection, K = 8192: 6% slower).
-constexpr int64_t kSplitLongK = 16384;
 int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co) {
-    if (T <= 64 || T >= 256 || (split16_tiles(T, Co) && Ci < kSplitLongK)) return 1;
+    if (T <= 64 || T >= 256 || (split16_tiles(T, Co) && Ci < kLongK)) return 1;
     const int64_t tiles = ((T + 127) / 128) * ((Co + 127) / 128);
     int64_t S = kCus / tiles;
     const int64_t nks = round_up_k(Ci) / 64;   // 64-byte K steps of the split kernel
