@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
     if (g == 0) dx[t] = d;
 }
 
-// Rows longer than 256 threads x 16 vectors: amax pass, then a second read.
+// Rows longer than 256 threads x 32 vectors: amax pass, then a second read.
 __global__ __launch_bounds__(256) void quant_act_long_kernel(
     const uint16_t* __restrict__ x, int64_t Ci, int64_t ldx,
     uint8_t* __restrict__ qx, int64_t ldq, float* __restrict__ dx) {
@@ -164,7 +164,8 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t Ci, int64_t ld
         case 2: return launch_act<256, 2>(x, T, Ci, ldx, qx, ldq, dx, s);
         case 4: return launch_act<256, 4>(x, T, Ci, ldx, qx, ldq, dx, s);
         case 8: return launch_act<256, 8>(x, T, Ci, ldx, qx, ldq, dx, s);
-        default: return launch_act<256, 16>(x, T, Ci, ldx, qx, ldq, dx, s);
+        case 16: return launch_act<256, 16>(x, T, Ci, ldx, qx, ldq, dx, s);
+        default: return launch_act<256, 32>(x, T, Ci, ldx, qx, ldq, dx, s);
     }
 }
 

@@ -78,12 +78,15 @@ EPILOGUE_CI, EPILOGUE_CO = 4112, 528
 PITCHED_T = [70, 300]                # Ci = 528, Co = 208
 PITCHED_CI, PITCHED_CO = 528, 208
 
-# Activation rows longer than one workgroup holds in registers (the two-pass
-# kernel): (T, Ci).
-LONG_ROW_CASES = [(7, 40960)]
+# Long activation rows, with the row maxima placed anywhere, the last row's
+# in its last vector: (T, Ci).  40960 and 65536: 32 vectors per thread in
+# registers; 65552: longer than one workgroup holds (the two-pass kernel).
+LONG_ROW_CASES = [(7, 40960), (4, 65536), (7, 65552)]
 
-# Row lengths of the exhaustive (x, amax) quantizer check.
-EXHAUSTIVE_CI = [512, 1024, 2048, 4096, 8192, 16384, 24576, 28672, 32768]
+# Row lengths of the exhaustive (x, amax) quantizer check: every launch shape
+# of rows of 256 or more vectors (the amax values are dealt to the lengths in
+# order, so the longest bucket gets the largest ones).
+EXHAUSTIVE_CI = [512, 1024, 2048, 4096, 8192, 16384, 24576, 28672, 65536]
 
 
 def gemm_shapes():

@@ -259,10 +259,10 @@ def test_quant_act_exhaustive_pairs():
 
 @pytest.mark.parametrize("T,Ci", ps.LONG_ROW_CASES)
 def test_quant_act_long_rows(T, Ci):
-    """Rows longer than one workgroup holds in registers (amax pass, then a
-    second read): codes and scales bit-exact, with each row's largest
-    magnitude placed in a different part of the row, the last row's in the
-    last 16-byte vector."""
+    """Long rows (32 vectors per thread in registers, and rows longer than
+    one workgroup holds: amax pass, then a second read): codes and scales
+    bit-exact, with each row's largest magnitude placed in a different part
+    of the row, the last row's in the last 16-byte vector."""
     note(f"long-row quant_act T={T} Ci={Ci}")
     rng = np.random.default_rng(Ci + T)
     x = workloads.random_bf16(rng, T, Ci, 1.0)
