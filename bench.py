@@ -922,7 +922,11 @@ def main():
     if not args.only and not args.no_judged:
         del xs, wts, qxs, dxs, pws, out, out2, ws
         torch.cuda.empty_cache()
-        judged = judged_shapes(stream)
+        try:
+            judged = judged_shapes(stream)
+        except Exception as e:      # the step's own line is still printed
+            print(f"judged_shapes failed: {e!r}", file=sys.stderr, flush=True)
+            judged = {"error": repr(e)}
 
     gemm_flops = 2.0 * T * Ci * Co
     w_bytes = 3.0 * Ci * Co + 4.0 * Co
@@ -996,7 +1000,11 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, args.cpu_seconds)
+        try:
+            result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, args.cpu_seconds)
+        except Exception as e:      # the step's own line is still printed
+            print(f"cpu_baseline failed: {e!r}", file=sys.stderr, flush=True)
+            result["cpu_baseline"] = {"error": repr(e)}
     print(json.dumps(no_nan(result)), flush=True)
 
 
