@@ -27,6 +27,12 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// An 8-byte store with the non-temporal cache hint.
+__device__ __forceinline__ void store_nt(uint2* p, uint2 v) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
+
 // Loads of rows held as 8 or more vectors per thread carry the non-temporal
 // hint (X is read once); measured faster there, slower for short rows.
 template <int VPT>
@@ -84,10 +90,19 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
     const float d = scale_from_amax(__uint_as_float(amax_bits << 16));
     const Divisor dv = make_divisor(d);
     uint2* qr = reinterpret_cast<uint2*>(qx + t * ldq);
+    // Rows of 256 or more vectors store their codes with the non-temporal
+    // hint: 4-8% faster with every input and output streamed from HBM (rows
+    // of 4096-28672 elements); with an output buffer the memory-side cache
+    // already holds, it was 0.5-4% slower.
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
         const int64_t c = (int64_t)j * G + g;
-        if (c < nchunk) qr[c] = quantize8(v[j], dv);
+        if (c < nchunk) {
+            if constexpr (G == 256)
+                store_nt(qr + c, quantize8(v[j], dv));
+            else
+                qr[c] = quantize8(v[j], dv);
+        }
     }
     if (g == 0) dx[t] = d;
 }
