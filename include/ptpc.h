@@ -129,11 +129,12 @@ ptpc_status ptpc_gemm(const uint8_t* qx, int64_t ldq, const float* dx,
 
 /*
  * Workspace that lets ptpc_gemm_ws split K across workgroups: nonzero only
- * for token counts whose output tiles are too few to occupy the GPU (65..255
- * tokens with few output columns, except where ptpc_gemm already splits K
- * inside each workgroup of 64x64 tiles: up to 128 tokens when those tiles
- * need no more rounds of the GPU than larger ones), then 4 * S * T * Co
- * bytes for S K ranges.
+ * where output tiles are too few to occupy the GPU -- 65..255 tokens with few
+ * output columns (except where ptpc_gemm already splits K inside each
+ * workgroup of 64x64 tiles: up to 128 tokens when those tiles need no more
+ * rounds of the GPU than larger ones), and 256 tokens or more with Ci >= 12288
+ * when fewer than 128 tiles of 256x256 cover the output -- then 4 * S * T * Co
+ * bytes for S K ranges (at most 64 MiB).
  */
 size_t ptpc_gemm_workspace_bytes(int64_t T, int64_t Ci, int64_t Co);
 
@@ -164,12 +165,12 @@ ptpc_status ptpc_gemm_ws(const uint8_t* qx, int64_t ldq, const float* dx,
  * ptpc_gemm_workspace_bytes(T, Ci, Co) is 0 this is exactly ptpc_gemm.
  * Shapes whose split needs more than PTPC_NOALLOC_SCRATCH_BYTES return
  * PTPC_ERR_UNSUPPORTED before anything is launched (the current split plan
- * never needs more: at most 16 MiB by construction).  Calls that overlap on
+ * never needs more: at most 64 MiB by construction).  Calls that overlap on
  * one GPU (different streams, or threads) share the scratch and race; calls
  * in one stream are ordered and safe.  The first call on a device looks up
  * the scratch's device address (PTPC_ERR_HIP if that fails).
  */
-#define PTPC_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define PTPC_NOALLOC_SCRATCH_BYTES (64u << 20)
 ptpc_status ptpc_gemm_noalloc(const uint8_t* qx, int64_t ldq, const float* dx,
                               const void* w_packed, const float* dw, int64_t T,
                               int64_t Ci, int64_t Co, void* out, int64_t ldo,

@@ -275,7 +275,7 @@ def gemm_ws(qx, dx, pw: PackedWeight, out=None, workspace=None, stream=None):
 
 
 # Scratch bytes the library holds per GPU for gemm_noalloc (include/ptpc.h).
-NOALLOC_SCRATCH_BYTES = 16 << 20
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def gemm_noalloc(qx, dx, pw: PackedWeight, out=None, stream=None):

@@ -16,6 +16,8 @@ constexpr int64_t kCus = 256;
 // on the workspace form splits the K-split 64x64 tile shapes too, and its
 // split kernel's weight fills carry the non-temporal hint.
 constexpr int64_t kLongK = 16384;
+// K from which the workspace form splits K for 256 tokens and more.
+constexpr int64_t kSplitK256 = 12288;
 
 // K extent of the packed weight: whole 128-byte K tiles.
 inline int64_t round_up_k(int64_t Ci) { return (Ci + 127) / 128 * 128; }
@@ -85,8 +87,8 @@ hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, c
 
 // The no-allocation split-K form: its scratch size, and the device address
 // of the current device's copy of the scratch array (looked up once per
-// device).
-constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+// device).  The split plan needs at most 64 MiB (see gemm_splitk_plan).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace ptpc

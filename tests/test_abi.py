@@ -137,6 +137,14 @@ def test_gemm_validation(L):
     assert L.ptpc_gemm_workspace_bytes(128, 8192, 57344) == 0           # 448 tiles
     assert L.ptpc_gemm_workspace_bytes(128, 8192, 8192) == 0            # K split in-workgroup
     assert L.ptpc_gemm_workspace_bytes(128, 28672, 8192) == 4 * 4 * 128 * 8192  # long K: split
+    # from 256 tokens: 256x256 tiles, S = 256 // tiles (<= 8), K >= 12288 only
+    assert L.ptpc_gemm_workspace_bytes(256, 28672, 8192) == 8 * 4 * 256 * 8192   # 32 tiles
+    assert L.ptpc_gemm_workspace_bytes(1024, 28672, 8192) == 2 * 4 * 1024 * 8192  # 128 tiles
+    assert L.ptpc_gemm_workspace_bytes(1024, 14336, 4096) == 4 * 4 * 1024 * 4096  # 64 tiles
+    assert L.ptpc_gemm_workspace_bytes(1024, 8192, 8192) == 0            # short K
+    assert L.ptpc_gemm_workspace_bytes(2048, 28672, 8192) == 0           # 256 tiles
+    assert L.ptpc_gemm_workspace_bytes(300, 1024, 256) == 0              # short K
+    assert L.ptpc_gemm_workspace_bytes(300, 2048 * 6, 256) == 8 * 4 * 300 * 256   # >= 8 steps each
     g = L.ptpc_gemm_ws
     assert g(A, 8192, B, C, D, 128, 8192, 10240, E, 10240, NULL, 0, None) == 1
     assert g(A, 8192, B, C, D, 128, 8192, 10240, E, 10240, D, need - 16, None) == 2
@@ -205,13 +213,18 @@ assert r == [5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 0], r
 
 def test_noalloc_scratch_covers_every_split(L):
     """ptpc_gemm_noalloc's per-GPU scratch holds the partial sums of every
-    shape the split-K plan splits (16 MiB by construction), and the call
-    validates like ptpc_gemm (no compute call here)."""
+    shape the split-K plan splits (16 MiB by construction below 256 tokens,
+    64 MiB from 256 on), and the call validates like ptpc_gemm (no compute
+    call here)."""
     import scaled_gemm_amd as sg
-    assert sg.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert sg.NOALLOC_SCRATCH_BYTES == 64 << 20
     worst = max(L.ptpc_gemm_workspace_bytes(T, Ci, Co) for T in range(65, 256)
                 for Ci in (2048, 8192, 28672) for Co in range(16, 66000, 16))
-    assert 0 < worst <= sg.NOALLOC_SCRATCH_BYTES
+    assert 0 < worst <= 16 << 20
+    worst = max(L.ptpc_gemm_workspace_bytes(T, Ci, Co)
+                for T in list(range(256, 1100, 7)) + [1536, 2048, 4096, 8192, 16384]
+                for Ci in (8192, 12288, 14336, 28672, 65536) for Co in range(16, 66000, 48))
+    assert 16 << 20 < worst <= sg.NOALLOC_SCRATCH_BYTES
     f = L.ptpc_gemm_noalloc
     assert f(A, 256, B, C, D, 0, 256, 512, E, 512, None) == 0
     assert f(A, 256, B, C, D, 4, 256, 500, E, 512, None) == 3

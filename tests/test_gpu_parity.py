@@ -412,6 +412,61 @@ def test_gemm_ws_split_k_ragged():
     assert np.array_equal(a, b), "split-K not deterministic"
 
 
+def test_gemm_ws_split_k_256_ragged():
+    """From 256 tokens on with K >= 12288 the workspace form runs 256x256
+    tiles of the 16x16x128 kernel over K ranges: here 8 ranges of 13 steps
+    of 128 bytes, the last one 6 steps ending in a 16-byte K tail, rows
+    ragged (300 = 256 + 44) and columns ragged (528 = 2 x 256 + 16).  Whole
+    output against the oracle, deterministic, workspace contents ignored."""
+    T, Ci, Co = 300, 12304, 528
+    need = sg.gemm_workspace_bytes(T, Ci, Co)
+    assert need == 8 * 4 * T * Co
+    note(f"split-K 256x256 ragged T={T} Ci={Ci} Co={Co}")
+    rng = np.random.default_rng(37)
+    x = workloads.random_bf16(rng, T, Ci, 1.0)
+    x[:, ::89] = workloads.f32_to_bf16_bits(workloads.bf16_bits_to_f32(x[:, ::89]) * np.float32(30))
+    x[:, -3:] = workloads.f32_to_bf16_bits(workloads.bf16_bits_to_f32(x[:, -3:]) * np.float32(20))
+    w = workloads.random_bf16(rng, Ci, Co, 0.02)
+    qx, dx = sg.quant_act(bits_to_dev(x))
+    pw = sg.quant_weight(bits_to_dev(w))
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")     # NaN-pattern garbage
+    o = sg.gemm_ws(qx, dx, pw, out=nan_filled(T, Co), workspace=ws)
+    no_nan(o, "split-K 256x256 ragged")
+    a = dev_to_bits(o)
+    b = dev_to_bits(sg.gemm_ws(qx, dx, pw))
+    qx_o, dx_o = oracle.quant_act(x)
+    qw_o, dw_o = oracle.quant_weight(w)
+    ref = oracle.apply_scales(oracle.gemm_exact(qx_o, qw_o), dx_o, dw_o)
+    check_close(a, ref, "split-K 256x256 ragged")
+    assert np.array_equal(a, b), "split-K not deterministic"
+
+
+def test_gemm_ws_long_k_256_plus():
+    """The 70B down projection (K = 28672) at 256 tokens (32 tiles of
+    256x256, 8 K ranges) and 1024 tokens (128 tiles, 2 ranges) through
+    ptpc_gemm_ws: every output written, sampled outputs against the oracle,
+    within a bf16 ulp of ptpc_gemm (another fp32 summation order)."""
+    shape, x, w = workloads.make("70b_down", T=1024)
+    pw = sg.quant_weight(bits_to_dev(w))
+    qw_o, dw_o = oracle.quant_weight(w)
+    for T, S in ((256, 8), (1024, 2)):
+        xs = np.ascontiguousarray(x[:T])
+        assert sg.gemm_workspace_bytes(T, shape.Ci, shape.Co) == S * 4 * T * shape.Co
+        note(f"split-K 70b down T={T} S={S}")
+        qx, dx = sg.quant_act(bits_to_dev(xs))
+        o = sg.gemm_ws(qx, dx, pw, out=nan_filled(T, shape.Co))
+        no_nan(o, f"70b down T={T} split-K")
+        out = dev_to_bits(o)
+        plain = dev_to_bits(sg.gemm(qx, dx, pw))
+        qx_o, dx_o = oracle.quant_act(xs)
+        rows, cols = sample_indices(T, shape.Co, 3000, seed=7)
+        ref = oracle_sampled_ref(qx_o, dx_o, qw_o, dw_o, rows, cols)
+        check_close(out[rows, cols], ref, f"70b down T={T} split-K (sampled)")
+        d = np.abs(bf16_f32(out) - bf16_f32(plain))
+        assert d.max() <= 2.0 ** -7 * np.abs(bf16_f32(plain)).max()
+        del qx, dx
+
+
 def test_gemm_ws_sweep_t128():
     """The 70B layers at 128 tokens through ptpc_gemm_ws (QKV: 3 K ranges;
     down, K = 28672: 4; O, whose 64x64 tiles split K inside the workgroup,
