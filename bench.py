@@ -525,7 +525,9 @@ def judged_shapes(stream, only=None):
     than 768 MiB between two uses of a copy); the median round.  The GEMM's
     rounds are back-to-back launches; the activation quantizer's (3-130 us
     kernels, shorter than the host's per-call cost at the smaller shapes)
-    replay the launches captured in a HIP graph."""
+    replay the launches captured in a HIP graph.  Where the workspace form
+    splits K (ptpc_gemm_ws; the 70B down projection at 1024 tokens), it is
+    timed the same way, partial sums and their reduction included."""
     import torch
 
     import scaled_gemm_amd as sg
@@ -568,6 +570,21 @@ def judged_shapes(stream, only=None):
         g_ms = graph_ms(gemm, reps_g, stream)
         a_ms = graph_ms(act, reps_a, stream)
         flops = 2.0 * T * Ci * Co
+        ws_rec = {}
+        ws_bytes = sg.gemm_workspace_bytes(T, Ci, Co)
+        if ws_bytes:
+            wsb = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+
+            def gemm_ws(i):
+                sg.gemm_ws(qxs[i % n], dxs[i % n], pws[i % n], out=out, workspace=wsb)
+
+            for i in range(2 * n):
+                gemm_ws(i)
+            w_ms = graph_ms(gemm_ws, reps_g, stream)
+            ws_rec = {"gemm_ws_ms": round(w_ms, 4),
+                      "gemm_ws_splits": ws_bytes // (4 * T * Co),
+                      "gemm_ws_frac_fp8_peak": round(flops / w_ms / 1e9 / PEAK_FP8_TFLOPS, 4)}
+            del wsb
         res.append({
             "shape": f"{name}_T{T}", "T": T, "Ci": Ci, "Co": Co,
             "gemm_kernel": sg.gemm_kernel(T, Ci, Co),
@@ -577,6 +594,7 @@ def judged_shapes(stream, only=None):
             "quant_act_ms": round(a_ms, 4),
             "quant_act_gbs": round(act_bytes(T, Ci) / a_ms / 1e6, 1),
             "quant_act_frac_hbm": round(act_bytes(T, Ci) / a_ms / 1e6 / PEAK_HBM_GBS, 4),
+            **ws_rec,
             "input_copies": {"gemm": n, "quant_act": nx},
         })
         print(f"# judged {name} T={T}: gemm {res[-1]['gemm_frac_fp8_peak']:.3f} of FP8 peak, "
