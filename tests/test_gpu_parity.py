@@ -441,6 +441,29 @@ def test_gemm_ws_split_k_256_ragged():
     assert np.array_equal(a, b), "split-K not deterministic"
 
 
+def test_gemm_ws_split_k_256_max_k():
+    """The 256x256 split at the contract's K limit (Ci = 2^17 - 16): 8 K
+    ranges of 128 steps, the last ending 16 bytes short of a whole step;
+    rows 260 = 256 + 4, columns 144 (one ragged column tile).  Whole output
+    against the oracle."""
+    T, Ci, Co = 260, (1 << 17) - 16, 144
+    need = sg.gemm_workspace_bytes(T, Ci, Co)
+    assert need == 8 * 4 * T * Co
+    note(f"split-K 256x256 max K T={T} Ci={Ci} Co={Co}")
+    rng = np.random.default_rng(41)
+    x = workloads.random_bf16(rng, T, Ci, 1.0)
+    x[:, -5:] = workloads.f32_to_bf16_bits(workloads.bf16_bits_to_f32(x[:, -5:]) * np.float32(25))
+    w = workloads.random_bf16(rng, Ci, Co, 0.02)
+    qx, dx = sg.quant_act(bits_to_dev(x))
+    pw = sg.quant_weight(bits_to_dev(w))
+    o = sg.gemm_ws(qx, dx, pw, out=nan_filled(T, Co))
+    no_nan(o, "split-K 256x256 max K")
+    qx_o, dx_o = oracle.quant_act(x)
+    qw_o, dw_o = oracle.quant_weight(w)
+    ref = oracle.apply_scales(oracle.gemm_exact(qx_o, qw_o), dx_o, dw_o)
+    check_close(dev_to_bits(o), ref, "split-K 256x256 max K")
+
+
 def test_gemm_ws_long_k_256_plus():
     """The 70B down projection (K = 28672) at 256 tokens (32 tiles of
     256x256, 8 K ranges) and 1024 tokens (128 tiles, 2 ranges) through
