@@ -62,6 +62,16 @@ GemmPlan gemm_plan(int64_t T, int64_t Ci, int64_t Co) {
                 best = c.plan;
             }
         }
+        // 128x128 tiles that leave CUs idle (256..~600 tokens with few output
+        // columns): 64x128 tiles of the 32x32x64 kernel instead.  Each moves a
+        // quarter fewer operand bytes, and two of its workgroups share a CU
+        // (56 KB of LDS, 136 registers per lane; the 16x16x128 kernel's
+        // 128x128 workgroup needs 264), so up to 512 run at once.  Cold-timed:
+        // the 70B O / QKV / down and 8B down layers at 256 tokens 1.45 / 1.24 /
+        // 1.53 / 1.56x faster, the 8B down layer at 384 and 512 tokens 1.56x,
+        // the 70B O and down layers at 384 tokens 1.04x and level.
+        if (best == GemmPlan::k16_128x128 && tiles(128, 128) < kCus && tiles(64, 128) <= 2 * kCus)
+            return GemmPlan::k32_64x128;
         return best;
     }
     if (T > 64) {

@@ -27,8 +27,15 @@ FULL_CASES = [
     ("ragged", 513, 512, 2064),
     ("ragged", 600, 144, 22000),
     ("ragged", 500, 144, 28656),
-    # 128-byte K steps run in periods of 6, the rest one by one: 12, 7 and 11
-    # steps (remainders 0, 1 and 5; the cases above cover 2, 3 and 4)
+    # the 16x16x128 tiled kernel runs its 128-byte K steps in periods of 6,
+    # the rest one by one: 12, 7 and 11 steps (remainders 0, 1 and 5; the
+    # other cases cover 2, 3 and 4), on 128x256 tiles with ragged rows and
+    # columns
+    ("ragged", 280, 1536, 16400),
+    ("ragged", 272, 880, 16656),
+    ("ragged", 520, 1392, 8208),
+    # the same K extents at 256+ tokens with few output columns: 64x128
+    # tiles of the 32x32x64 kernel
     ("ragged", 280, 1536, 528),
     ("ragged", 272, 880, 1296),
     ("ragged", 520, 1392, 400),
@@ -54,9 +61,12 @@ TILE_CASES = [
     (1024, 880, 10240),     # 192x256 tiles with a partial last row tile, 7 K steps
     (256, 1040, 40944),     # 256x160 tiles with a partial last column tile, 9 K steps
     (1024, 752, 14336),     # 256x224 tiles, 6 K steps
-    (512, 16400, 1024),     # 128x128 tiles, long K: 129 K steps
-    (512, 1040, 4096),      # 128x128 tiles at 256+ tokens, 9 K steps
-    (256, 131072 - 16, 512),  # K near the contract's 2^17 limit, 128x128 tiles, 1024 K steps
+    (512, 16400, 8192),     # 128x128 tiles at 256+ tokens, long K: 129 K steps
+    (512, 1040, 8192),      # 128x128 tiles at 256+ tokens, 9 K steps
+    # where 128x128 tiles would leave CUs idle at 256+ tokens: 64x128 tiles of
+    # the 32x32x64 kernel (two workgroups per CU)
+    (512, 16400, 1024),     # long K: 257 K steps of 64 bytes
+    (256, 131072 - 16, 512),  # K near the contract's 2^17 limit: 2048 K steps
 ]
 
 CONFIG_CASES = ["8b_gate_up", "70b_down"]
@@ -72,11 +82,17 @@ PER_TENSOR_CASES = [("tiny", 16, 256, 512), ("ragged", 48, 272, 10256),
                     ("ragged", 100, 528, 1040)]   # the K-split 64x64 tiles, scalar scales
 
 # Epilogue edge values: T picks the kernel family (Ci = 4112, Co = 528).
-EPILOGUE_T = [16, 100, 200, 512]
-EPILOGUE_CI, EPILOGUE_CO = 4112, 528
+# (T, Ci, Co) of the epilogue edge-value test: T picks the kernel family --
+# 16 the few-token kernel, 100 the K-split 64x64 tiles, 200 the 64x64 tiles
+# of the 32x32x64 kernel (and 4 K ranges through the workspace form), 512
+# its 64x128 tiles at 256+ tokens, 520 x 8208 columns the 16x16x128 tiled
+# kernel (128x256 tiles).
+EPILOGUE_CASES = [(16, 4112, 528), (100, 4112, 528), (200, 4112, 528), (512, 4112, 528),
+                  (520, 1040, 8208)]
 
-PITCHED_T = [70, 300]                # Ci = 528, Co = 208
-PITCHED_CI, PITCHED_CO = 528, 208
+# (T, Ci, Co) of the pitched-buffer test: the K-split 64x64 tiles, the 64x128
+# tiles of the 32x32x64 kernel, the 16x16x128 tiled kernel.
+PITCHED_CASES = [(70, 528, 208), (300, 528, 208), (520, 528, 8208)]
 
 # Long activation rows, with the row maxima placed anywhere, the last row's
 # in its last vector: (T, Ci).  40960 and 65536: 32 vectors per thread in
@@ -101,8 +117,8 @@ def gemm_shapes():
         out += [(T, Ci, Co) for T in workloads.SWEEP_T]
     out += [(T, *workloads.SWEEP_LAYERS[layer]) for layer, T in EXTRA_SWEEP_CASES]
     out += [(T, Ci, Co) for _, T, Ci, Co in PER_TENSOR_CASES]
-    out += [(T, EPILOGUE_CI, EPILOGUE_CO) for T in EPILOGUE_T]
-    out += [(T, PITCHED_CI, PITCHED_CO) for T in PITCHED_T]
+    out += list(EPILOGUE_CASES)
+    out += list(PITCHED_CASES)
     return out
 
 

@@ -153,13 +153,10 @@ def same_bits(got, want, what):
                            f"{[(int(t), int(o), hex(got[t, o]), hex(want[t, o])) for t, o in bad[:4]]}")
 
 
-# T picks the kernel family: 16 the few-token kernel, 100 the K-split 64x64
-# tiles, 200 the 128x128 / 64x128 tiles (and 4 K ranges through the workspace
-# form), 512 the 16x16x128 tile kernel.
+# The shape picks the kernel family (see parity_shapes.EPILOGUE_CASES).
 @pytest.mark.gpu
-@pytest.mark.parametrize("T", ps.EPILOGUE_T)
-def test_epilogue_edge_values(gpu_lib, T):
-    Ci, Co = ps.EPILOGUE_CI, ps.EPILOGUE_CO
+@pytest.mark.parametrize("T,Ci,Co", ps.EPILOGUE_CASES)
+def test_epilogue_edge_values(gpu_lib, T, Ci, Co):
     note(f"epilogue edges T={T} Ci={Ci} Co={Co}")
     x, w, dx, dw = edge_case(T, Ci, Co, seed=T)
     qx_o, qw_o, want, ws_want, want_bf = expected(x, w, dx, dw)

@@ -328,12 +328,12 @@ def test_empty_and_zero_extents():
     assert sg.gemm(q1, d1, pw1).shape == (3, 0)
 
 
-@pytest.mark.parametrize("T", ps.PITCHED_T)
-def test_pitched_inputs_and_outputs(T):
-    """Row pitches larger than the extents (views into wider buffers); 70
-    tokens run the K-split 64x64 tiles, 300 the 128-byte-step tiled kernel."""
+@pytest.mark.parametrize("T,Ci,Co", ps.PITCHED_CASES)
+def test_pitched_inputs_and_outputs(T, Ci, Co):
+    """Row pitches larger than the extents (views into wider buffers): the
+    K-split 64x64 tiles, the 64x128 tiles at 256+ tokens and the 128-byte-step
+    tiled kernel."""
     rng = np.random.default_rng(12)
-    Ci, Co = ps.PITCHED_CI, ps.PITCHED_CO
     xb = workloads.random_bf16(rng, T, Ci + 40, 1.0)
     wb = workloads.random_bf16(rng, Ci, Co + 24, 0.02)
     xd = bits_to_dev(xb)[:, :Ci]
