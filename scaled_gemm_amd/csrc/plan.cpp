@@ -39,7 +39,8 @@ GemmPlan gemm_plan(int64_t T, int64_t Ci, int64_t Co) {
         // 256x256 tiles leave CUs idle or a badly filled last round (70B QKV
         // at 1024 tokens: 240 tiles of 192x256 for 160 of 256x256; O and down:
         // 256 tiles of 128x256; gate_up: 1024 of 256x224 for 3.5 rounds of
-        // 256x256; 256..600 tokens of the 8192-column layers: 128x128).
+        // 256x256; 384..600 tokens of the 8192-column layers: 128x128, and
+        // fewer tokens the 64x128 tiles below).
         struct Cand {
             GemmPlan plan;
             int64_t bm, bn;
