@@ -139,15 +139,18 @@ const char* gemm_plan_name(GemmPlan p) {
 //   From 256 tokens on, with K of at least kSplitK256 bytes: 256x256 tiles
 // (the 16x16x128 kernel), K cut into S ranges of at least 8 steps of 128
 // bytes, S = the largest that keeps tiles x S within one round of the CUs
-// (at most 8).  ptpc_gemm's own tile there is smaller (128x128 or 128x256,
-// the K loop at 44-55% of the 256x256 one's rate per flop) or leaves CUs
-// idle; cold-timed through ptpc_gemm_ws, partial sums and their reduction
-// included: the 70B down projection (K = 28672) at 256 / 512 / 768 / 1024
-// tokens 2.1 / 1.4 / 1.14 / 1.08x faster, the 8B one (K = 14336) at
-// 256 / 512 / 1024 tokens 2.2 / 1.8 / 1.24x and level at 2048, K = 12288 at
-// 1024 tokens 1.18x; K = 8192 (the 70B O projection at 512..1024 tokens)
-// 5-17% slower, so shorter K is not split.  S x tiles <= 256 bounds the
-// workspace: 4 * S * T * Co <= 4 * 256 * 256 * 256 bytes = 64 MiB.
+// (at most 8).  ptpc_gemm's own tiles there are smaller (64x128, 128x128 or
+// 128x256: more operand bytes per flop) or leave CUs idle.  Cold-timed
+// against ptpc_gemm in one run, partial sums and their reduction included:
+// the 70B down projection (K = 28672) at 256 / 512 / 768 / 1024 tokens
+// 1.28 / 1.42 / 1.13 / 1.07x faster; the 8B one (K = 14336) at 256 and 1024
+// tokens 1.39 / 1.16x and K = 12288 at 1024 tokens 1.13x, but the 8B one at
+// 512 tokens, where ptpc_gemm's 64x128 tiles already give every CU one, 0.86x
+// (8 ranges), and at 2048 tokens (2 ranges) 0.97x.  So below kLongK the split
+// needs at least 4 ranges and a ptpc_gemm grid that leaves CUs idle.  K =
+// 8192 (the 70B O projection at 512..1024 tokens) lost 5-17%, so shorter K is
+// not split.  S x tiles <= 256 bounds the workspace: 4 * S * T * Co <= 4 *
+// 256 * 256 * 256 bytes = 64 MiB.
 int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co) {
     if (T >= 256) {
         if (Ci < kSplitK256) return 1;
@@ -155,6 +158,12 @@ int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co) {
         const int64_t n128 = round_up_k(Ci) / 128;
         if (S > n128 / 8) S = n128 / 8;
         if (S > 8) S = 8;
+        if (Ci < kLongK) {
+            if (S < 4) return 1;
+            if (gemm_plan(T, Ci, Co) == GemmPlan::k32_64x128 &&
+                ((T + 63) / 64) * ((Co + 127) / 128) >= kCus)
+                return 1;
+        }
         return S < 2 ? 1 : (int)S;
     }
     if (T <= 64 || (split16_tiles(T, Co) && Ci < kLongK)) return 1;

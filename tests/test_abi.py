@@ -141,6 +141,10 @@ def test_gemm_validation(L):
     assert L.ptpc_gemm_workspace_bytes(256, 28672, 8192) == 8 * 4 * 256 * 8192   # 32 tiles
     assert L.ptpc_gemm_workspace_bytes(1024, 28672, 8192) == 2 * 4 * 1024 * 8192  # 128 tiles
     assert L.ptpc_gemm_workspace_bytes(1024, 14336, 4096) == 4 * 4 * 1024 * 4096  # 64 tiles
+    assert L.ptpc_gemm_workspace_bytes(256, 14336, 4096) == 8 * 4 * 256 * 4096    # 16 tiles
+    assert L.ptpc_gemm_workspace_bytes(512, 14336, 4096) == 0    # K < 16384, 64x128 fill the GPU
+    assert L.ptpc_gemm_workspace_bytes(2048, 14336, 4096) == 0   # K < 16384, 2 ranges only
+    assert L.ptpc_gemm_workspace_bytes(2048, 28672, 4096) == 2 * 4 * 2048 * 4096  # long K: 2
     assert L.ptpc_gemm_workspace_bytes(1024, 8192, 8192) == 0            # short K
     assert L.ptpc_gemm_workspace_bytes(2048, 28672, 8192) == 0           # 256 tiles
     assert L.ptpc_gemm_workspace_bytes(300, 1024, 256) == 0              # short K
