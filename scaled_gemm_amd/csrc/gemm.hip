@@ -136,9 +136,7 @@ __device__ __forceinline__ void timeline_mark(int k) {
 // share 12 operand blocks per K step.
 constexpr int kXcds = 8;
 constexpr int kGroupN = 8;
-__device__ __forceinline__ void tile_of(int i, int gm, int gn, int& tm, int& tn) {
-    const int n = gm * gn;
-    if (n % kXcds == 0) i = (i % kXcds) * (n / kXcds) + i / kXcds;
+__device__ __forceinline__ void tile_group_of(int i, int gm, int gn, int& tm, int& tn) {
     const int group = i / (kGroupN * gm);
     const int first_n = group * kGroupN;
     const int width = (gn - first_n < kGroupN) ? gn - first_n : kGroupN;
@@ -148,6 +146,26 @@ __device__ __forceinline__ void tile_of(int i, int gm, int gn, int& tm, int& tn)
     // scalar (a descriptor in vector registers costs a loop per load).
     tm = __builtin_amdgcn_readfirstlane(r / width);
     tn = __builtin_amdgcn_readfirstlane(first_n + r % width);
+}
+__device__ __forceinline__ void tile_of(int i, int gm, int gn, int& tm, int& tn) {
+    const int n = gm * gn;
+    if (n % kXcds == 0) i = (i % kXcds) * (n / kXcds) + i / kXcds;
+    tile_group_of(i, gm, gn, tm, tn);
+}
+// Split-K grids of the 16x16x128 kernel (S K ranges of every tile): the XCD
+// remap runs over all S x tiles workgroups, range-major, so that an XCD's
+// share is a run of consecutive tiles of one K range, grouped as in an
+// unsplit grid (range-minor, an XCD held tiles of every range, which share
+// no operand blocks: the 70B down projection at 512 / 1024 tokens, 4 / 2
+// ranges, ran 11% / 3% slower).  S = 1 gives tile_of's mapping.  Returns the
+// range; `tile` gets the tile's index in the group order.
+__device__ __forceinline__ int split_of(int b, int splits, int ntiles, int& tile) {
+    const int total = ntiles * splits;
+    int L = b;
+    if (total % kXcds == 0) L = (b % kXcds) * (total / kXcds) + b / kXcds;
+    const int split = __builtin_amdgcn_readfirstlane(L / ntiles);
+    tile = __builtin_amdgcn_readfirstlane(L - split * ntiles);
+    return split;
 }
 
 // The pipeline.  K advances in 64-byte steps; each step is one MFMA K
@@ -654,7 +672,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
     const int lg = lane >> 4;
     const int gm = (int)((T + BM - 1) / BM), gn = (int)((Co + BN - 1) / BN);
     const int ntiles = gm * gn;
-    const int split = (int)blockIdx.x / ntiles;
+    int tile_lin;
+    const int split = split_of((int)blockIdx.x, splits, ntiles, tile_lin);
     const int nks = (int)(Kp / KS);
     const int per = (nks + splits - 1) / splits;
     const int ks0 = split * per < nks ? split * per : nks;
@@ -668,7 +687,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
     // bl * 1024.  Offsets are 32-bit (the descriptors span less than 4 GB)
     // and branch-free.
     int tm, tn;
-    tile_of((int)blockIdx.x - split * ntiles, gm, gn, tm, tn);
+    tile_group_of(tile_lin, gm, gn, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
     const int64_t a_rows = (T - m0 < BM) ? (T - m0) : BM;
