@@ -85,6 +85,9 @@ def parse(argv=None):
                         "--only <kernel> --copy-calibration-mb run into the traffic record of "
                         "--traffic-kernel and exit (no GPU needed)")
     p.add_argument("--traffic-kernel", default="gemm_fused", choices=sorted(TRAFFIC))
+    p.add_argument("--shapes", default=None, metavar="T:Ci:Co,...",
+                   help="ptpc_gemm and ptpc_gemm_ws on these shapes (inputs drawn on the GPU, "
+                        "rotated, graph-timed in interleaved rounds); one JSON line per shape")
     p.add_argument("--timeline", action="store_true",
                    help="per-workgroup phases of the tiled GEMM (timeline debug build) on the "
                         "bench workload and the judged shapes; one JSON line per shape")
@@ -604,6 +607,67 @@ def judged_shapes(stream, only=None):
     return res
 
 
+def shapes_mode(args):
+    """ptpc_gemm and ptpc_gemm_ws on the given (T, Ci, Co): the 70B layers'
+    activation structure (Student-t x log-normal rows) and normal weights,
+    drawn on the GPU, rotated over copies (more than 768 MiB between two uses
+    of one); after a warm-up, three interleaved rounds of graph replays of
+    each form, the best round.  The workspace form's time includes its
+    partial sums and their reduction where it splits K."""
+    import torch
+
+    import scaled_gemm_amd as sg
+    import workloads
+
+    stream = torch.cuda.current_stream()
+    dev = torch.device("cuda:0")
+    for k, spec in enumerate(args.shapes.split(",")):
+        T, Ci, Co = (int(v) for v in spec.split(":"))
+        x = workloads.device_activation("student_lognormal", T, Ci, 9000 + k, dev)
+        w = workloads.device_weight(200, k, Ci, Co, 0.01, dev)
+        pw = sg.quant_weight(w)
+        del w
+        qx, dx = sg.quant_act(x)
+        del x
+        n = n_sets(T * Ci + pw.data.numel())
+        pws = [pw] + [sg.PackedWeight(pw.data.clone(), pw.dw.clone(), Ci, Co) for _ in range(n - 1)]
+        qxs = [qx] + [qx.clone() for _ in range(n - 1)]
+        dxs = [dx] + [dx.clone() for _ in range(n - 1)]
+        out = torch.empty((T, Co), dtype=torch.bfloat16, device=dev)
+        ws_bytes = sg.gemm_workspace_bytes(T, Ci, Co)
+        wsb = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+
+        def gemm(i):
+            sg.gemm(qxs[i % n], dxs[i % n], pws[i % n], out=out)
+
+        def gemm_ws(i):
+            sg.gemm_ws(qxs[i % n], dxs[i % n], pws[i % n], out=out, workspace=wsb)
+
+        reps = max(2 * n, 10)
+        for i in range(2 * n):
+            gemm(i)
+            gemm_ws(i)
+        t = {"gemm": [], "gemm_ws": []}
+        for _ in range(3):
+            t["gemm"].append(graph_ms(gemm, reps, stream))
+            t["gemm_ws"].append(graph_ms(gemm_ws, reps, stream))
+        g, w_ = min(t["gemm"]), min(t["gemm_ws"])
+        flops = 2.0 * T * Ci * Co
+        print(json.dumps({
+            "shape": f"T{T}_Ci{Ci}_Co{Co}", "T": T, "Ci": Ci, "Co": Co,
+            "gemm_kernel": sg.gemm_kernel(T, Ci, Co),
+            "gemm_us": round(g * 1e3, 1),
+            "gemm_frac_fp8_peak": round(flops / g / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "gemm_ws_splits": ws_bytes // (4 * T * Co) if ws_bytes else 1,
+            "gemm_ws_us": round(w_ * 1e3, 1),
+            "gemm_ws_frac_fp8_peak": round(flops / w_ / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "ws_speedup": round(g / w_, 3),
+            "input_copies": n,
+        }), flush=True)
+        del qx, dx, pw, pws, qxs, dxs, out, wsb
+        torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------------------
 # timeline of the tiled GEMM (debug build)
 # ---------------------------------------------------------------------------
@@ -740,6 +804,9 @@ def main():
         return
     if args.timeline:
         timeline(args)
+        return
+    if args.shapes:
+        shapes_mode(args)
         return
     if args.traffic_from:
         rec = traffic_record(args.traffic_from[0], args.traffic_from[1], args.workload,
