@@ -132,7 +132,9 @@ ptpc_status ptpc_gemm(const uint8_t* qx, int64_t ldq, const float* dx,
  * where output tiles are too few to occupy the GPU -- 65..255 tokens with few
  * output columns (except where ptpc_gemm already splits K inside each
  * workgroup of 64x64 tiles: up to 128 tokens when those tiles need no more
- * rounds of the GPU than larger ones), and 256 tokens or more with Ci >= 16384
+ * rounds of the GPU than larger ones; at 129..255 tokens with Ci >= 16384 or
+ * where ptpc_gemm runs 128x128 tiles, one 256-row tile per weight slab), and
+ * 256 tokens or more with Ci >= 16384
  * when fewer than 128 tiles of 256x256 cover the output (with 12288 <= Ci <
  * 16384 only for a split of at least 4 ranges where ptpc_gemm's own tiles
  * leave CUs idle) -- then 4 * S * T * Co bytes for S K ranges (at most

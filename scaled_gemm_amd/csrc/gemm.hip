@@ -1689,10 +1689,10 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
 hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                               const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                               int64_t ldo, float* ws, int splits, hipStream_t s) {
-    // 256 tokens and more: 256x256 tiles of the 16x16x128 kernel; fewer:
-    // 128x128 tiles of the 32x32x64 kernel
+    // 256x256 tiles of the 16x16x128 kernel (from 256 tokens on, and some
+    // shapes of 129..255 tokens) or 128x128 tiles of the 32x32x64 kernel
     const hipError_t e =
-        T >= 256 ? launch_tiles16<256, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, ws, s,
+        gemm_split_tiles256(T, Ci, Co) ? launch_tiles16<256, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, ws, s,
                                                   kTokenChannelScales, splits)
         : Ci >= kLongK ? launch_tiles<128, 128, 2, 2, 4, true>(qx, ldq, dx, wp, dw, T, Ci, Co, out,
                                                                ldo, ws, s, kTokenChannelScales, splits)

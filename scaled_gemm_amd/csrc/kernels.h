@@ -81,6 +81,7 @@ hipError_t launch_gemm_unfused_bf16(const uint8_t* qx, int64_t ldq, const float*
 // writing S fp32 partial slices [S][T][Co] to ws before one reduce + scale
 // pass into bf16 `out`.
 int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co);
+bool gemm_split_tiles256(int64_t T, int64_t Ci, int64_t Co);
 hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                               const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                               int64_t ldo, float* ws, int splits, hipStream_t s);

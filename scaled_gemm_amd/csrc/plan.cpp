@@ -151,13 +151,35 @@ const char* gemm_plan_name(GemmPlan p) {
 // 8192 (the 70B O projection at 512..1024 tokens) lost 5-17%, so shorter K is
 // not split.  S x tiles <= 256 bounds the workspace: 4 * S * T * Co <= 4 *
 // 256 * 256 * 256 bytes = 64 MiB.
+// K ranges for 256x256 tiles: the most that keep tiles x S within one round
+// of the CUs, at most 8, each at least 8 steps of 128 bytes.
+static int64_t splits256(int64_t T, int64_t Ci, int64_t Co) {
+    int64_t S = kCus / (((T + 255) / 256) * ((Co + 255) / 256));
+    const int64_t n128 = round_up_k(Ci) / 128;
+    if (S > n128 / 8) S = n128 / 8;
+    if (S > 8) S = 8;
+    return S;
+}
+
+// Whether the split runs 256x256 tiles of the 16x16x128 kernel (else 128x128
+// tiles of the 32x32x64 kernel).  From 256 tokens on always; at 129..255
+// tokens, where 128-row tiles read every weight byte twice and one 256-row
+// tile reads it once, for long K or where ptpc_gemm itself would run 128x128
+// tiles (cold, through ptpc_gemm_ws: the 70B down projection at 200 / 255
+// tokens 88.0 -> 70.5 / 81.0 -> 78.4 us, the 70B QKV projection at 200
+// tokens 51.1 -> 39.7 us; where ptpc_gemm runs 64-row tiles with K < 16384
+// -- the 70B O layer at 144 / 200 tokens, QKV at 160, 8B down at 192 -- the
+// 256x256 split was 3-20% slower).
+bool gemm_split_tiles256(int64_t T, int64_t Ci, int64_t Co) {
+    if (T >= 256) return true;
+    if (T <= 128 || splits256(T, Ci, Co) < 2) return false;
+    return Ci >= kLongK || gemm_plan(T, Ci, Co) == GemmPlan::k16_128x128;
+}
+
 int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co) {
     if (T >= 256) {
         if (Ci < kSplitK256) return 1;
-        int64_t S = kCus / (((T + 255) / 256) * ((Co + 255) / 256));
-        const int64_t n128 = round_up_k(Ci) / 128;
-        if (S > n128 / 8) S = n128 / 8;
-        if (S > 8) S = 8;
+        const int64_t S = splits256(T, Ci, Co);
         if (Ci < kLongK) {
             if (S < 4) return 1;
             if (gemm_plan(T, Ci, Co) == GemmPlan::k32_64x128 &&
@@ -166,6 +188,7 @@ int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co) {
         }
         return S < 2 ? 1 : (int)S;
     }
+    if (gemm_split_tiles256(T, Ci, Co)) return (int)splits256(T, Ci, Co);
     if (T <= 64 || (split16_tiles(T, Co) && Ci < kLongK)) return 1;
     const int64_t tiles = ((T + 127) / 128) * ((Co + 127) / 128);
     int64_t S = kCus / tiles;

@@ -145,6 +145,11 @@ def test_gemm_validation(L):
     assert L.ptpc_gemm_workspace_bytes(512, 14336, 4096) == 0    # K < 16384, 64x128 fill the GPU
     assert L.ptpc_gemm_workspace_bytes(2048, 14336, 4096) == 0   # K < 16384, 2 ranges only
     assert L.ptpc_gemm_workspace_bytes(2048, 28672, 4096) == 2 * 4 * 2048 * 4096  # long K: 2
+    # 129..255 tokens: one 256-row tile (the weight read once) for long K or
+    # where ptpc_gemm would run 128x128 tiles, else 128x128 split tiles
+    assert L.ptpc_gemm_workspace_bytes(200, 28672, 8192) == 8 * 4 * 200 * 8192   # long K
+    assert L.ptpc_gemm_workspace_bytes(200, 8192, 10240) == 6 * 4 * 200 * 10240  # 128x128 plan
+    assert L.ptpc_gemm_workspace_bytes(200, 8192, 8192) == 2 * 4 * 200 * 8192    # 128x128 split
     assert L.ptpc_gemm_workspace_bytes(1024, 8192, 8192) == 0            # short K
     assert L.ptpc_gemm_workspace_bytes(2048, 28672, 8192) == 0           # 256 tiles
     assert L.ptpc_gemm_workspace_bytes(300, 1024, 256) == 0              # short K
@@ -217,14 +222,17 @@ assert r == [5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 0], r
 
 def test_noalloc_scratch_covers_every_split(L):
     """ptpc_gemm_noalloc's per-GPU scratch holds the partial sums of every
-    shape the split-K plan splits (16 MiB by construction below 256 tokens,
-    64 MiB from 256 on), and the call validates like ptpc_gemm (no compute
-    call here)."""
+    shape the split-K plan splits (64 MiB by construction: 128x128 splits
+    need at most 16 MiB, 256x256 splits at most 64 MiB), and the call
+    validates like ptpc_gemm (no compute call here)."""
     import scaled_gemm_amd as sg
     assert sg.NOALLOC_SCRATCH_BYTES == 64 << 20
-    worst = max(L.ptpc_gemm_workspace_bytes(T, Ci, Co) for T in range(65, 256)
+    worst = max(L.ptpc_gemm_workspace_bytes(T, Ci, Co) for T in range(65, 129)
                 for Ci in (2048, 8192, 28672) for Co in range(16, 66000, 16))
     assert 0 < worst <= 16 << 20
+    worst = max(L.ptpc_gemm_workspace_bytes(T, Ci, Co) for T in range(129, 256)
+                for Ci in (2048, 8192, 28672) for Co in range(16, 66000, 16))
+    assert 16 << 20 < worst <= sg.NOALLOC_SCRATCH_BYTES
     worst = max(L.ptpc_gemm_workspace_bytes(T, Ci, Co)
                 for T in list(range(256, 1100, 7)) + [1536, 2048, 4096, 8192, 16384]
                 for Ci in (8192, 12288, 14336, 28672, 65536) for Co in range(16, 66000, 48))

@@ -464,6 +464,51 @@ def test_gemm_ws_split_k_256_max_k():
     check_close(dev_to_bits(o), ref, "split-K 256x256 max K")
 
 
+def test_gemm_ws_split_k_256_rows_129_255():
+    """At 129..255 tokens with long K the workspace form runs one 256-row
+    tile per weight slab (256x256 tiles, rows past T out of range): 200
+    tokens, K 16400 (8 ranges of 17 steps of 128 bytes, the last 10 steps
+    with a 16-byte tail), 528 columns.  Whole output against the oracle; then
+    the 70B QKV (where ptpc_gemm runs 128x128 tiles: 6 ranges) and down
+    (8 ranges) layers at 200 tokens, sampled, within a bf16 ulp-scale of
+    ptpc_gemm."""
+    T, Ci, Co = 200, 16400, 528
+    need = sg.gemm_workspace_bytes(T, Ci, Co)
+    assert need == 8 * 4 * T * Co
+    note(f"split-K 256x256 at {T} tokens: Ci={Ci} Co={Co}")
+    rng = np.random.default_rng(43)
+    x = workloads.random_bf16(rng, T, Ci, 1.0)
+    x[:, ::71] = workloads.f32_to_bf16_bits(workloads.bf16_bits_to_f32(x[:, ::71]) * np.float32(30))
+    w = workloads.random_bf16(rng, Ci, Co, 0.02)
+    qx, dx = sg.quant_act(bits_to_dev(x))
+    pw = sg.quant_weight(bits_to_dev(w))
+    o = sg.gemm_ws(qx, dx, pw, out=nan_filled(T, Co))
+    no_nan(o, "split-K 256x256 at 200 tokens")
+    qx_o, dx_o = oracle.quant_act(x)
+    qw_o, dw_o = oracle.quant_weight(w)
+    ref = oracle.apply_scales(oracle.gemm_exact(qx_o, qw_o), dx_o, dw_o)
+    check_close(dev_to_bits(o), ref, "split-K 256x256 at 200 tokens")
+    del qx, dx, pw
+    for layer, S in (("qkv", 6), ("down", 8)):
+        shape, x, w = workloads.make("70b_sweep", T=200, layer=layer)
+        assert sg.gemm_workspace_bytes(200, shape.Ci, shape.Co) == S * 4 * 200 * shape.Co
+        note(f"split-K 70b {layer} T=200 S={S}")
+        qx, dx = sg.quant_act(bits_to_dev(x))
+        pw = sg.quant_weight(bits_to_dev(w))
+        o = sg.gemm_ws(qx, dx, pw, out=nan_filled(200, shape.Co))
+        no_nan(o, f"70b {layer} T=200 split-K")
+        out = dev_to_bits(o)
+        plain = dev_to_bits(sg.gemm(qx, dx, pw))
+        qx_o, dx_o = oracle.quant_act(x)
+        qw_o, dw_o = oracle.quant_weight(w)
+        rows, cols = sample_indices(200, shape.Co, 3000, seed=9)
+        ref = oracle_sampled_ref(qx_o, dx_o, qw_o, dw_o, rows, cols)
+        check_close(out[rows, cols], ref, f"70b {layer} T=200 split-K (sampled)")
+        d = np.abs(bf16_f32(out) - bf16_f32(plain))
+        assert d.max() <= 2.0 ** -7 * np.abs(bf16_f32(plain)).max()
+        del qx, dx, pw
+
+
 def test_gemm_ws_long_k_256_plus():
     """The 70B down projection (K = 28672) at 256 tokens (32 tiles of
     256x256, 8 K ranges) and 1024 tokens (128 tiles, 2 ranges) through
