@@ -585,7 +585,7 @@ def judged_shapes(stream, only=None):
                 gemm_ws(i)
             w_ms = graph_ms(gemm_ws, reps_g, stream)
             ws_rec = {"gemm_ws_ms": round(w_ms, 4),
-                      "gemm_ws_splits": ws_bytes // (4 * T * Co),
+                      "gemm_ws_splits": sg.gemm_ws_splits(T, Ci, Co),
                       "gemm_ws_frac_fp8_peak": round(flops / w_ms / 1e9 / PEAK_FP8_TFLOPS, 4)}
             del wsb
         res.append({
@@ -658,7 +658,7 @@ def shapes_mode(args):
             "gemm_kernel": sg.gemm_kernel(T, Ci, Co),
             "gemm_us": round(g * 1e3, 1),
             "gemm_frac_fp8_peak": round(flops / g / 1e9 / PEAK_FP8_TFLOPS, 4),
-            "gemm_ws_splits": ws_bytes // (4 * T * Co) if ws_bytes else 1,
+            "gemm_ws_splits": sg.gemm_ws_splits(T, Ci, Co),
             "gemm_ws_us": round(w_ * 1e3, 1),
             "gemm_ws_frac_fp8_peak": round(flops / w_ / 1e9 / PEAK_FP8_TFLOPS, 4),
             "ws_speedup": round(g / w_, 3),

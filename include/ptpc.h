@@ -138,7 +138,9 @@ ptpc_status ptpc_gemm(const uint8_t* qx, int64_t ldq, const float* dx,
  * when fewer than 128 tiles of 256x256 cover the output (with 12288 <= Ci <
  * 16384 only for a split of at least 4 ranges where ptpc_gemm's own tiles
  * leave CUs idle) -- then 4 * S * T * Co bytes for S K ranges (at most
- * 64 MiB).
+ * 64 MiB), except for splits of 2 ranges over 256x256 tiles, which need
+ * n * (262144 + 16) bytes for the n = ceil(T/256) * ceil(Co/256) output
+ * tiles (at most 128 tiles, 32 MiB).
  */
 size_t ptpc_gemm_workspace_bytes(int64_t T, int64_t Ci, int64_t Co);
 
@@ -149,8 +151,13 @@ size_t ptpc_gemm_workspace_bytes(int64_t T, int64_t Ci, int64_t Co);
  * Otherwise K is cut into S ranges, each workgroup writes the fp32 partial
  * sums of one range of one output tile to the workspace, and one more pass
  * adds the S partials in range order and applies the same epilogue
- * bf16((sum * dx[t]) * dw[o]).  The result is deterministic; it can differ
- * from ptpc_gemm's in the last bf16 bit (another fp32 summation order).
+ * bf16((sum * dx[t]) * dw[o]).  With S = 2 over 256x256 tiles there is no
+ * second pass: of the two workgroups of a tile, the one that finishes first
+ * publishes its sums in the workspace, the other adds them to its own and
+ * applies the epilogue (per-tile counters in the workspace, cleared by the
+ * call; a workgroup only ever waits for one that is already running).  The
+ * result is deterministic and the same in both forms; it can differ from
+ * ptpc_gemm's in the last bf16 bit (another fp32 summation order).
  * PTPC_ERR_NULL for a missing, PTPC_ERR_SHAPE for a too small workspace.
  */
 ptpc_status ptpc_gemm_ws(const uint8_t* qx, int64_t ldq, const float* dx,
@@ -260,6 +267,10 @@ const char* ptpc_gemm_kernel(int64_t T, int64_t Ci, int64_t Co);
 
 /* Kernel of ptpc_quant_act for T rows of Ci elements. */
 const char* ptpc_quant_act_kernel(int64_t T, int64_t Ci);
+
+/* Number of K ranges ptpc_gemm_ws and ptpc_gemm_noalloc cut K into for a
+ * shape (1: no split, the call is ptpc_gemm's; 0: a shape the calls reject). */
+int ptpc_gemm_ws_splits(int64_t T, int64_t Ci, int64_t Co);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ EXPORTS = (
     "ptpc_gemm_unfused_workspace_bytes", "ptpc_gemm_unfused",
     "ptpc_gemm_unfused_bf16_workspace_bytes", "ptpc_gemm_unfused_bf16", "ptpc_tensor_scale",
     "ptpc_quant_act_static", "ptpc_quant_weight_static", "ptpc_gemm_tensor",
-    "ptpc_gemm_kernel", "ptpc_quant_act_kernel",
+    "ptpc_gemm_kernel", "ptpc_quant_act_kernel", "ptpc_gemm_ws_splits",
 )
 
 _lib = None
@@ -91,6 +91,8 @@ def lib():
         L.ptpc_gemm_kernel.argtypes = [I, I, I]
         L.ptpc_quant_act_kernel.restype = ctypes.c_char_p
         L.ptpc_quant_act_kernel.argtypes = [I, I]
+        L.ptpc_gemm_ws_splits.restype = ctypes.c_int
+        L.ptpc_gemm_ws_splits.argtypes = [I, I, I]
         _lib = L
     return _lib
 
@@ -183,6 +185,11 @@ def gemm_kernel(T: int, Ci: int, Co: int):
     """Name of the GEMM kernel ptpc_gemm launches for this shape (None if none)."""
     r = lib().ptpc_gemm_kernel(T, Ci, Co)
     return r.decode() if r is not None else None
+
+
+def gemm_ws_splits(T: int, Ci: int, Co: int) -> int:
+    """K ranges ptpc_gemm_ws / ptpc_gemm_noalloc use for this shape (1: no split)."""
+    return int(lib().ptpc_gemm_ws_splits(T, Ci, Co))
 
 
 def quant_act_kernel(T: int, Ci: int):

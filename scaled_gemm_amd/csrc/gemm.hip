@@ -49,6 +49,13 @@ namespace ptpc {
 
 constexpr int BK = 64;          // K bytes per step (one MFMA K step)
 constexpr uint32_t kOutOfRange = 0x80000000u;
+// Bound on the sleeps of the two-range fix-up's wait (gemm16_kernel): about
+// 2^20 x 64 clocks, far beyond the microseconds the other range needs to
+// publish its sums.
+constexpr int kFixupSpins = 1 << 20;
+// Cache-policy bits of a buffer load: sc1, device-coherent (reads memory,
+// not a stale line of this XCD's L2).
+constexpr int kSc1 = 16;
 
 // LDS bank swizzles (64 banks of 4 bytes; an operand read has 16 consecutive
 // rows of one logical 16-byte chunk in flight per LDS cycle).
@@ -615,12 +622,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(
 //   them right after issue, as in compiler-scheduled code).
 // The K loop runs whole periods of 6 steps, then the remaining 0-5 steps,
 // each behind a uniform branch; fills for steps past the data read zeros.
-template <int BM, int BN, int WM, int WN, bool FUSED>
+template <int BM, int BN, int WM, int WN, bool FUSED, bool FIXUP = false>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
     const uint8_t* __restrict__ qx, int64_t ldq, const float* __restrict__ dx,
     const uint8_t* __restrict__ wp, int64_t Kp, const float* __restrict__ dw,
     int64_t T, int64_t Ci, int64_t Co, void* __restrict__ out, int64_t ldo, int scale_mode,
-    int splits) {
+    int splits, float* __restrict__ part) {
+    static_assert(!FIXUP || FUSED, "the two-range fix-up ends in the fused epilogue");
     constexpr int KS = 128;                          // K bytes per step
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -914,6 +922,60 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
         timeline_mark(2);
     }
 
+    // Published sums of the other K range (two-range fix-up), read with
+    // device-coherent loads (unused otherwise).
+    float* const tslot = FIXUP ? part + (int64_t)tile_lin * BM * BN : part;
+    const __amdgpu_buffer_rsrc_t rpart =
+        make_rsrc(tslot, FIXUP ? (uint32_t)(BM * BN * sizeof(float)) : 0u);
+    if constexpr (FIXUP) {
+        // Two K ranges per tile, joined without a second pass.  Each
+        // workgroup takes a ticket on its tile's record once its K loop is
+        // done.  Ticket 0 publishes its fp32 sums in the tile's slot of
+        // `part` (lane order: one 1 KB run per wave and accumulator tile),
+        // writes them back from its XCD's L2 to memory, raises the record's
+        // flag and exits.  Ticket 1 waits for that flag -- set by a
+        // workgroup that is already past its own K loop, so the wait ends
+        // whatever the order of dispatch -- and its epilogue adds the
+        // published sums, read with device-coherent (sc1) loads, to its own.
+        // No L2 invalidation: that would drop the operand lines of the
+        // workgroups of its XCD still in their K loops (with one, the 70B O
+        // projection at 1024 tokens ran 1.4x slower).  With two terms the sum
+        // does not depend on which range arrives first (IEEE addition
+        // commutes): the result is range 0 + range 1 in any timing.  The wait
+        // is bounded (kFixupSpins sleeps of ~64 clocks) so that no fault
+        // elsewhere can keep the kernel from exiting.  Records are 4 words
+        // per tile after the slots, cleared before the launch.
+        uint32_t* const rec = reinterpret_cast<uint32_t*>(part + (int64_t)ntiles * BM * BN) +
+                              4 * tile_lin;
+        volatile uint32_t* const bcast = reinterpret_cast<volatile uint32_t*>(b_s2);
+        if (tid == 0)
+            *bcast = __hip_atomic_fetch_add(rec, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const uint32_t ticket = __builtin_amdgcn_readfirstlane(*bcast);
+        if (ticket == 0) {
+            float* const slot = tslot + wave * (MT * NT * 256) + lane * 4;
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    *reinterpret_cast<v4f*>(slot + (i * NT + j) * 256) = acc[i][j];
+            // every wave's stores have reached its L2 before the one
+            // write-back that the flag's release makes
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0)
+                __hip_atomic_store(rec + 1, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        if (tid == 0) {
+            int spins = 0;
+            while (__hip_atomic_load(rec + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
+                   ++spins < kFixupSpins)
+                __builtin_amdgcn_s_sleep(1);
+        }
+        __syncthreads();
+    }
+
     // Epilogue.  The weight slab is the MFMA's first operand, so the 16x16
     // accumulator tile is out^T: in lane l, element e holds token row l % 16
     // of the slab and column 4 * (l / 16) + e.  As in gemm_kernel, the bf16
@@ -947,17 +1009,36 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
         const int64_t e_rows = (T - m0 < BM) ? (T - m0) : BM;
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc(reinterpret_cast<uint16_t*>(out) + m0 * ldo, (uint32_t)(e_rows * ldo * 2));
+        // Two-range fix-up: the other range's sums of slab i, loaded one
+        // slab ahead of their use.
+        v4f pv[2][FIXUP ? NT : 1];
+        auto load_pv = [&](int i, int b) __attribute__((always_inline)) {
+            if constexpr (FIXUP) {
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const uint32_t off =
+                        (uint32_t)((wave * (MT * NT * 256) + (i * NT + j) * 256 + lane * 4) * 4);
+                    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rpart, off, 0, kSc1);
+                    pv[b][j] = v4f{__int_as_float(v.x), __int_as_float(v.y),
+                                   __int_as_float(v.z), __int_as_float(v.w)};
+                }
+            }
+        };
+        load_pv(0, 0);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
+            if (i + 1 < MT) load_pv(i + 1, (i + 1) & 1);
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const float sx = sxv[i];
                 const float4 sw = swv[j];
+                v4f a = acc[i][j];
+                if constexpr (FIXUP) a += pv[i & 1][j];
                 uint2 pk;
-                pk.x = f32x2_to_bf16x2_rne((acc[i][j][0] * sx) * sw.x,
-                       (acc[i][j][1] * sx) * sw.y);
-                pk.y = f32x2_to_bf16x2_rne((acc[i][j][2] * sx) * sw.z,
-                       (acc[i][j][3] * sx) * sw.w);
+                pk.x = f32x2_to_bf16x2_rne((a[0] * sx) * sw.x,
+                       (a[1] * sx) * sw.y);
+                pk.y = f32x2_to_bf16x2_rne((a[2] * sx) * sw.z,
+                       (a[3] * sx) * sw.w);
                 *reinterpret_cast<uint2*>(stage + l16 * PITCH +
                                           (slot_of(l16, 2 * j + (lg >> 1)) << 4) +
                                           (lg & 1) * 8) = pk;
@@ -1607,12 +1688,20 @@ static hipError_t launch_tiles16(const uint8_t* qx, int64_t ldq, const float* dx
     const int64_t Kp = round_up_k(Ci);
     if (fp32_out == nullptr) {
         hipLaunchKernelGGL((gemm16_kernel<BM, BN, WM, WN, true>), grid, dim3(WM * WN * 64), 0, s,
-                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out, ldo, mode, 1);
+                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)out, ldo, mode, 1,
+                           (float*)nullptr);
     } else {
         hipLaunchKernelGGL((gemm16_kernel<BM, BN, WM, WN, false>), grid, dim3(WM * WN * 64), 0, s,
-                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)fp32_out, Co, 0, splits);
+                           qx, ldq, dx, wp, Kp, dw, T, Ci, Co, (void*)fp32_out, Co, 0, splits,
+                           (float*)nullptr);
     }
     return hipGetLastError();
+}
+
+// Clears the tile records of the two-range fix-up.
+__global__ __launch_bounds__(256) void clear_records_kernel(uint32_t* __restrict__ p, int n) {
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = 0u;
 }
 
 static hipError_t launch_tiles16s(const uint8_t* qx, int64_t ldq, const float* dx,
@@ -1689,6 +1778,18 @@ hipError_t launch_gemm(const uint8_t* qx, int64_t ldq, const float* dx, const ui
 hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                               const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                               int64_t ldo, float* ws, int splits, hipStream_t s) {
+    if (gemm_split_fixup(T, Ci, Co)) {
+        // Two K ranges of 256x256 tiles joined inside the GEMM kernel: tile
+        // slots of fp32 sums, then 4 record words per tile, cleared first.
+        const int ntiles = (int)(((T + 255) / 256) * ((Co + 255) / 256));
+        uint32_t* const rec = reinterpret_cast<uint32_t*>(ws + (int64_t)ntiles * 256 * 256);
+        hipLaunchKernelGGL(clear_records_kernel, dim3((unsigned)((4 * ntiles + 255) / 256)),
+                           dim3(256), 0, s, rec, 4 * ntiles);
+        hipLaunchKernelGGL((gemm16_kernel<256, 256, 2, 2, true, true>), dim3((unsigned)(2 * ntiles)),
+                           dim3(256), 0, s, qx, ldq, dx, wp, round_up_k(Ci), dw, T, Ci, Co,
+                           (void*)out, ldo, (int)kTokenChannelScales, 2, ws);
+        return hipGetLastError();
+    }
     // 256x256 tiles of the 16x16x128 kernel (from 256 tokens on, and some
     // shapes of 129..255 tokens) or 128x128 tiles of the 32x32x64 kernel
     const hipError_t e =

@@ -82,6 +82,13 @@ hipError_t launch_gemm_unfused_bf16(const uint8_t* qx, int64_t ldq, const float*
 // pass into bf16 `out`.
 int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co);
 bool gemm_split_tiles256(int64_t T, int64_t Ci, int64_t Co);
+// Two K ranges of 256x256 tiles: the ranges are joined inside the GEMM
+// kernel (the second to finish adds the first's published sums), so ws holds
+// one fp32 slot per tile plus a 4-word record per tile, and no reduction
+// pass follows.  Other splits write S slices [S][T][Co] and reduce them.
+bool gemm_split_fixup(int64_t T, int64_t Ci, int64_t Co);
+// Workspace bytes of the split plan (0: no split).
+size_t gemm_splitk_workspace_bytes(int64_t T, int64_t Ci, int64_t Co);
 hipError_t launch_gemm_splitk(const uint8_t* qx, int64_t ldq, const float* dx, const uint8_t* wp,
                               const float* dw, int64_t T, int64_t Ci, int64_t Co, uint16_t* out,
                               int64_t ldo, float* ws, int splits, hipStream_t s);

@@ -198,6 +198,20 @@ int gemm_splitk_plan(int64_t T, int64_t Ci, int64_t Co) {
     return S < 2 ? 1 : (int)S;
 }
 
+bool gemm_split_fixup(int64_t T, int64_t Ci, int64_t Co) {
+    return gemm_splitk_plan(T, Ci, Co) == 2 && gemm_split_tiles256(T, Ci, Co);
+}
+
+size_t gemm_splitk_workspace_bytes(int64_t T, int64_t Ci, int64_t Co) {
+    const int S = gemm_splitk_plan(T, Ci, Co);
+    if (S < 2) return 0;
+    if (gemm_split_fixup(T, Ci, Co)) {
+        const size_t tiles = (size_t)(((T + 255) / 256) * ((Co + 255) / 256));
+        return tiles * (256 * 256 * sizeof(float) + 4 * sizeof(uint32_t));
+    }
+    return (size_t)S * (size_t)T * (size_t)Co * sizeof(float);
+}
+
 static int pow2_ceil(int64_t v) {
     int p = 1;
     while (p < v) p <<= 1;

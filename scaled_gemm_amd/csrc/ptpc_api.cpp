@@ -159,8 +159,7 @@ size_t ptpc_gemm_workspace_bytes(int64_t T, int64_t Ci, int64_t Co) {
     if (T <= 0 || Ci <= 0 || Co <= 0 || Ci % 16 != 0 || Co % 16 != 0 || Ci > kMaxK ||
         T > kMaxExtent || Co > kMaxExtent || T * Co > kMaxOutputs)
         return 0;
-    const int S = ptpc::gemm_splitk_plan(T, Ci, Co);
-    return S > 1 ? (size_t)S * (size_t)T * (size_t)Co * sizeof(float) : 0;
+    return ptpc::gemm_splitk_workspace_bytes(T, Ci, Co);
 }
 
 ptpc_status ptpc_gemm_ws(const uint8_t* qx, int64_t ldq, const float* dx, const void* w_packed,
@@ -286,6 +285,13 @@ const char* ptpc_gemm_kernel(int64_t T, int64_t Ci, int64_t Co) {
         T > kMaxExtent || Co > kMaxExtent || T * Co > kMaxOutputs)
         return nullptr;
     return ptpc::gemm_plan_name(ptpc::gemm_plan(T, Ci, Co));
+}
+
+int ptpc_gemm_ws_splits(int64_t T, int64_t Ci, int64_t Co) {
+    if (T <= 0 || Ci <= 0 || Co <= 0 || Ci % 16 != 0 || Co % 16 != 0 || Ci > kMaxK ||
+        T > kMaxExtent || Co > kMaxExtent || T * Co > kMaxOutputs)
+        return 0;
+    return ptpc::gemm_splitk_plan(T, Ci, Co);
 }
 
 const char* ptpc_quant_act_kernel(int64_t T, int64_t Ci) {

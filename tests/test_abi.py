@@ -139,12 +139,20 @@ def test_gemm_validation(L):
     assert L.ptpc_gemm_workspace_bytes(128, 28672, 8192) == 4 * 4 * 128 * 8192  # long K: split
     # from 256 tokens: 256x256 tiles, S = 256 // tiles (<= 8), K >= 12288 only
     assert L.ptpc_gemm_workspace_bytes(256, 28672, 8192) == 8 * 4 * 256 * 8192   # 32 tiles
-    assert L.ptpc_gemm_workspace_bytes(1024, 28672, 8192) == 2 * 4 * 1024 * 8192  # 128 tiles
+    # two ranges over 256x256 tiles are joined in the GEMM kernel: one fp32
+    # slot of 256x256 per tile and a 16-byte record per tile
+    assert L.ptpc_gemm_workspace_bytes(1024, 28672, 8192) == 128 * (4 * 256 * 256 + 16)
     assert L.ptpc_gemm_workspace_bytes(1024, 14336, 4096) == 4 * 4 * 1024 * 4096  # 64 tiles
     assert L.ptpc_gemm_workspace_bytes(256, 14336, 4096) == 8 * 4 * 256 * 4096    # 16 tiles
     assert L.ptpc_gemm_workspace_bytes(512, 14336, 4096) == 0    # K < 16384, 64x128 fill the GPU
     assert L.ptpc_gemm_workspace_bytes(2048, 14336, 4096) == 0   # K < 16384, 2 ranges only
-    assert L.ptpc_gemm_workspace_bytes(2048, 28672, 4096) == 2 * 4 * 2048 * 4096  # long K: 2
+    assert L.ptpc_gemm_workspace_bytes(2048, 28672, 4096) == 128 * (4 * 256 * 256 + 16)  # long K: 2
+    assert L.ptpc_gemm_workspace_bytes(300, 16400, 10768) == 86 * (4 * 256 * 256 + 16)  # ragged: 2
+    # the split count behind those sizes (1: no split; 0: rejected shape)
+    sp = L.ptpc_gemm_ws_splits
+    assert [sp(1024, 28672, 8192), sp(256, 28672, 8192), sp(128, 8192, 10240),
+            sp(4096, 28672, 8192), sp(300, 16400, 10768)] == [2, 8, 3, 1, 2]
+    assert sp(0, 256, 256) == 0 and sp(16, 250, 256) == 0 and sp(16, 256, 0) == 0
     # 129..255 tokens: one 256-row tile (the weight read once) for long K or
     # where ptpc_gemm would run 128x128 tiles, else 128x128 split tiles
     assert L.ptpc_gemm_workspace_bytes(200, 28672, 8192) == 8 * 4 * 200 * 8192   # long K

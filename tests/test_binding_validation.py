@@ -18,7 +18,8 @@ class NoCompute:
     """The real library for size and kernel queries; any compute call fails."""
     QUERIES = {"ptpc_weight_packed_bytes", "ptpc_gemm_workspace_bytes",
                "ptpc_gemm_unfused_workspace_bytes", "ptpc_gemm_unfused_bf16_workspace_bytes",
-               "ptpc_gemm_kernel", "ptpc_quant_act_kernel", "ptpc_status_string"}
+               "ptpc_gemm_kernel", "ptpc_quant_act_kernel", "ptpc_gemm_ws_splits",
+               "ptpc_status_string"}
 
     def __init__(self, real):
         self.real = real

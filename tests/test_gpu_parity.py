@@ -519,7 +519,8 @@ def test_gemm_ws_long_k_256_plus():
     qw_o, dw_o = oracle.quant_weight(w)
     for T, S in ((256, 8), (1024, 2)):
         xs = np.ascontiguousarray(x[:T])
-        assert sg.gemm_workspace_bytes(T, shape.Ci, shape.Co) == S * 4 * T * shape.Co
+        assert sg.gemm_workspace_bytes(T, shape.Ci, shape.Co) == (
+            S * 4 * T * shape.Co if S > 2 else fixup_ws_bytes(T, shape.Co))
         note(f"split-K 70b down T={T} S={S}")
         qx, dx = sg.quant_act(bits_to_dev(xs))
         o = sg.gemm_ws(qx, dx, pw, out=nan_filled(T, shape.Co))
@@ -533,6 +534,66 @@ def test_gemm_ws_long_k_256_plus():
         d = np.abs(bf16_f32(out) - bf16_f32(plain))
         assert d.max() <= 2.0 ** -7 * np.abs(bf16_f32(plain)).max()
         del qx, dx
+
+
+def fixup_ws_bytes(T, Co):
+    """Workspace of a two-range split over 256x256 tiles: an fp32 slot of
+    256x256 per tile, then a 4-word record per tile."""
+    return ((T + 255) // 256) * ((Co + 255) // 256) * (4 * 256 * 256 + 16)
+
+
+def fixup_records(ws, T, Co):
+    """The per-tile records [tickets taken, published flag, 0, 0] a two-range
+    call leaves in its workspace."""
+    n = ((T + 255) // 256) * ((Co + 255) // 256)
+    rec = ws[n * 4 * 256 * 256:n * (4 * 256 * 256 + 16)].cpu().numpy()
+    return rec.view(np.uint32).reshape(n, 4)
+
+
+def test_gemm_ws_two_range_fixup():
+    """Two K ranges over 256x256 tiles, joined inside the GEMM kernel (the
+    range that finishes second adds the first's published sums): 300 tokens
+    (rows ragged: 256 + 44), K 16400 (65 + 64 steps of 128 bytes, a 16-byte
+    tail), 10768 columns (42 x 256 + 16): 86 tiles, 172 workgroups.  The
+    workspace starts as garbage (record words included); every output is
+    written, sampled outputs match the oracle, the whole output is within a
+    bf16 ulp-scale of ptpc_gemm, every tile's record shows both tickets taken
+    and the sums published, and a second call with other activations over
+    the same workspace gives that call's result, bit-identical to a call on
+    a fresh workspace."""
+    T, Ci, Co = 300, 16400, 10768
+    need = sg.gemm_workspace_bytes(T, Ci, Co)
+    assert need == fixup_ws_bytes(T, Co) == 86 * (4 * 256 * 256 + 16)
+    note(f"two-range fix-up T={T} Ci={Ci} Co={Co}")
+    rng = np.random.default_rng(47)
+    w = workloads.random_bf16(rng, Ci, Co, 0.02)
+    pw = sg.quant_weight(bits_to_dev(w))
+    qw_o, dw_o = oracle.quant_weight(w)
+    del w
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")     # NaN-pattern garbage
+    ws[86 * 4 * 256 * 256:] = 0x5A                                          # garbage records
+    for call, seed in ((1, 48), (2, 49)):
+        x = workloads.random_bf16(np.random.default_rng(seed), T, Ci, 1.0)
+        x[:, ::83] = workloads.f32_to_bf16_bits(
+            workloads.bf16_bits_to_f32(x[:, ::83]) * np.float32(30))
+        x[:, -4:] = workloads.f32_to_bf16_bits(
+            workloads.bf16_bits_to_f32(x[:, -4:]) * np.float32(20))
+        qx, dx = sg.quant_act(bits_to_dev(x))
+        o = sg.gemm_ws(qx, dx, pw, out=nan_filled(T, Co), workspace=ws)
+        no_nan(o, f"two-range fix-up call {call}")
+        out = dev_to_bits(o)
+        rec = fixup_records(ws, T, Co)
+        assert np.all(rec[:, 0] == 2) and np.all(rec[:, 1] == 1), f"records after call {call}"
+        fresh = dev_to_bits(sg.gemm_ws(qx, dx, pw))
+        assert np.array_equal(out, fresh), f"call {call} depends on the workspace it found"
+        plain = dev_to_bits(sg.gemm(qx, dx, pw))
+        d = np.abs(bf16_f32(out) - bf16_f32(plain))
+        assert d.max() <= 2.0 ** -7 * np.abs(bf16_f32(plain)).max()
+        qx_o, dx_o = oracle.quant_act(x)
+        rows, cols = sample_indices(T, Co, 4000, seed=call)
+        ref = oracle_sampled_ref(qx_o, dx_o, qw_o, dw_o, rows, cols)
+        check_close(out[rows, cols], ref, f"two-range fix-up call {call} (sampled)")
+        del qx, dx, x
 
 
 def test_gemm_ws_sweep_t128():
