@@ -42,7 +42,7 @@ MAX_SETS = 64
 TRAFFIC = {
     "gemm_fused": {"file": "gemm_fused_70b_down_traffic.json",
                    "sources": ("gemm.hip", "device_common.h"),
-                   "kernel": "gemm16_kernel<256, 256, 2, 2, true>"},
+                   "kernel": "gemm16_kernel<256, 256, 2, 2, true, false>"},
     "quant_act": {"file": "quant_act_70b_down_traffic.json",
                   "sources": ("quant.hip", "device_common.h"),
                   "kernel": "quant_act_kernel<256, 16>"},
