@@ -33,7 +33,10 @@ PIPELINED = {
     "gemm16_kernel<128,128,2,2>", "gemm16s_kernel", "gemm_kernel<64,64,2,2,4>",
     "gemm_kernel<64,128,2,2,4>", "gemm_kernel<128,128,2,2,4>", "gemm_kernel<32,64,1,2,4>",
 }
-SPLIT_K = (200, 4112, 400)
+# The split-K forms of ptpc_gemm_ws: 128x128 tiles of the 32x32x64 kernel
+# (4 K ranges, then the reduction pass), 256x256 tiles (8 ranges, reduction
+# pass), and two ranges of 256x256 tiles joined inside the kernel.
+SPLIT_K = [(200, 4112, 400, 4), (300, 12304, 528, 8), (1024, 16400, 8192, 2)]
 
 
 @pytest.fixture(scope="module")
@@ -105,15 +108,17 @@ def test_poison_build_equals_release(libs, T, Ci, Co):
     assert torch.equal(got2.view(torch.int16), ref2.view(torch.int16)), "two-step differs"
 
 
-def test_poison_build_split_k(libs):
+@pytest.mark.parametrize("T,Ci,Co,S", SPLIT_K)
+def test_poison_build_split_k(libs, T, Ci, Co, S):
     sg, L = libs
-    T, Ci, Co = SPLIT_K
     need = sg.gemm_workspace_bytes(T, Ci, Co)
-    assert need > 0
+    assert need > 0 and sg.gemm_ws_splits(T, Ci, Co) == S
+    note(f"lds poison split-K T={T} Ci={Ci} Co={Co} S={S}")
     qx, dx, pw = operands(sg, T, Ci, Co, seed=11)
     ref = sg.gemm_ws(qx, dx, pw)
     got = torch.full_like(ref, float("nan"))
     ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
     run_poison(L, "ptpc_gemm_ws", qx, dx, pw, got, p(ws), need)
     torch.cuda.synchronize()
+    assert not torch.isnan(got).any()
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
