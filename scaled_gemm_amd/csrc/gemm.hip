@@ -726,9 +726,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
     // asm) so that the compiler forms each fill's LDS address with one add
     // instead of holding one register per fill and slot across the loop.
     int wlds = wave * 1024;
+    // Rows past the tile's last row need no test of their own: the
+    // descriptors span exactly a_rows rows of A and b_rows columns of the
+    // packed weight, so their offsets fall outside and read as zero.
     auto issue_a = [&](int ks, int p, uint8_t* slot) __attribute__((always_inline)) {
         const int k0 = ks * KS;
-        const bool in = (a_r0 + p * NW * 8 < (int)a_rows) & (k0 + a_c16 < k_lim);
+        const bool in = k0 + a_c16 < k_lim;
         const uint32_t off =
             in ? a_lane + (uint32_t)(p * NW * 8) * (uint32_t)ldq + (uint32_t)k0 : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + wlds + p * NW * 1024),
@@ -737,7 +740,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
     auto issue_b = [&](int ks, int p, uint8_t* slot) __attribute__((always_inline)) {
         const int bl = wave + p * NW;
         const int blk = bl % BH, h = bl / BH;
-        const bool in = (bl < B_BLK) & (blk * 16 < (int)b_rows) & (ks < nsteps);
+        const bool in = (bl < B_BLK) & (ks < nsteps);
         const uint32_t off =
             in ? b_lane + ((uint32_t)(blk * 16) * (uint32_t)Kp + (uint32_t)(h * 1024 + ks * 2048))
                : kOutOfRange;
@@ -928,6 +931,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
         }(std::make_integer_sequence<int, P - 1>{});
         wait_counts<0, 0>();
         lds_barrier();
+        // The MFMAs are inline asm, invisible to the compiler's hazard
+        // tracking: 24 wait states after the last one, and every accumulator
+        // pinned behind them, so that no read of an accumulator (the
+        // epilogue's, or a copy the register allocator makes) comes sooner.
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) asm volatile("" : "+a"(acc[i][j]));
         timeline_mark(2);
     }
 
@@ -1001,6 +1013,12 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
     static_assert(!FUSED || NW * 16 * PITCH <= A_SLOT, "staging");
     auto slot_of = [](int r, int c) { return POW2 ? (c ^ ((r / RB) % NC)) : c; };
     if constexpr (FUSED) {
+        // Lane coordinates re-derived here (the empty asm hides where they
+        // come from), so that nothing the epilogue computes from them is
+        // hoisted above the K loop and held through it.
+        int elane = (int)threadIdx.x;
+        asm volatile("" : "+v"(elane));
+        const int lane = elane & 63, l16 = elane & 15, lg = (elane >> 4) & 3;
         float sxv[MT];
         float4 swv[NT];
 #pragma unroll
