@@ -1761,6 +1761,8 @@ static hipError_t launch_main(const uint8_t* qx, int64_t ldq, const float* dx, c
             return launch_tiles16<256, 160, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
         case GemmPlan::k16_128x256:
             return launch_tiles16<128, 256, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
+        case GemmPlan::k16_128x224:
+            return launch_tiles16<128, 224, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
         case GemmPlan::k16_128x128:
             return launch_tiles16<128, 128, 2, 2>(qx, ldq, dx, wp, dw, T, Ci, Co, out, ldo, fp32_out, s, ts);
         case GemmPlan::k16s_64x64:

@@ -43,7 +43,7 @@ hipError_t launch_unpack_weight(const uint8_t* packed, int64_t Ci, int64_t Co, u
 // The GEMM kernel and tile ptpc_gemm (and both two-step forms) launch for a
 // shape, chosen on the host from T, Ci and Co alone.
 enum class GemmPlan : int {
-    k16_256x256, k16_192x256, k16_256x224, k16_256x160, k16_128x256, k16_128x128,
+    k16_256x256, k16_192x256, k16_256x224, k16_256x160, k16_128x256, k16_128x128, k16_128x224,
     k16s_64x64, k32_64x64, k32_64x128, k32_128x128, k32_32x64,
     kDecode_2x2, kDecode_2x1, kDecode_1x2, kDecode_1x1,
 };

@@ -89,6 +89,16 @@ GemmPlan gemm_plan(int64_t T, int64_t Ci, int64_t Co) {
         if (split16_tiles(T, Co)) return GemmPlan::k16s_64x64;
         if (r64 <= r128 && r64 <= r64w) return GemmPlan::k32_64x64;
         if (r64w <= r128) return GemmPlan::k32_64x128;
+        // Wide layers whose 128x128 tiles need more than one round: one row
+        // tile of 224 columns (rows past T read as zero) where those fill
+        // more than half the CUs in one round -- the weight is read once,
+        // by every CU at once.  Cold-timed on the 70B gate_up layer (57344
+        // columns, 256 such tiles) at 96 / 128 / 160 / 200 / 255 tokens:
+        // 5 / 9 / 21 / 19 / 18% faster than 128x128 tiles; level at 72; on
+        // the 8B gate_up layer (128 tiles, half the CUs) 4-10% slower.
+        const int64_t wide = (Co + 223) / 224;
+        if (T > 80 && r128 > 1 && wide <= kCus && 2 * wide > kCus)
+            return T <= 128 ? GemmPlan::k16_128x224 : GemmPlan::k16_256x224;
         return GemmPlan::k16_128x128;   // the 16x16x128 kernel, 3-5% faster here (70B gate_up)
     }
     // Up to 64 tokens the weight stream decides.  The tiled kernel reads
@@ -115,6 +125,7 @@ const char* gemm_plan_name(GemmPlan p) {
         case GemmPlan::k16_256x160: return "gemm16_kernel<256,160,2,2>";
         case GemmPlan::k16_128x256: return "gemm16_kernel<128,256,2,2>";
         case GemmPlan::k16_128x128: return "gemm16_kernel<128,128,2,2>";
+        case GemmPlan::k16_128x224: return "gemm16_kernel<128,224,2,2>";
         case GemmPlan::k16s_64x64: return "gemm16s_kernel";
         case GemmPlan::k32_64x64: return "gemm_kernel<64,64,2,2,4>";
         case GemmPlan::k32_64x128: return "gemm_kernel<64,128,2,2,4>";

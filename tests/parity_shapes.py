@@ -61,6 +61,9 @@ TILE_CASES = [
     (1024, 880, 10240),     # 192x256 tiles with a partial last row tile, 7 K steps
     (256, 1040, 40944),     # 256x160 tiles with a partial last column tile, 9 K steps
     (1024, 752, 14336),     # 256x224 tiles, 6 K steps
+    # wide layers at 81..255 tokens: one row tile of 224 columns per weight slab
+    (100, 1040, 50192),     # 128x224 tiles, rows past T, a 16-column last tile, 9 K steps
+    (200, 1040, 50192),     # 256x224 tiles with a partial row tile, 9 K steps
     (512, 16400, 8192),     # 128x128 tiles at 256+ tokens, long K: 129 K steps
     (512, 1040, 8192),      # 128x128 tiles at 256+ tokens, 9 K steps
     # where 128x128 tiles would leave CUs idle at 256+ tokens: 64x128 tiles of

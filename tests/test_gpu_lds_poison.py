@@ -25,12 +25,13 @@ SHAPES = [
     (4096, 1648, 4096), (1536, 592, 8192), (1024, 880, 10240), (1024, 752, 14336),
     (256, 1040, 40944), (1024, 28672, 8192), (512, 16400, 1024), (100, 528, 1040),
     (120, 3344, 1040), (200, 144, 1040), (130, 272, 8208), (48, 272, 32784),
-    (20, 144, 32784), (200, 272, 36864),
+    (20, 144, 32784), (200, 272, 36864), (200, 272, 10240), (100, 272, 50192),
 ]
 PIPELINED = {
     "gemm16_kernel<256,256,2,2>", "gemm16_kernel<192,256,2,2>", "gemm16_kernel<256,224,4,1>",
     "gemm16_kernel<256,160,2,2>", "gemm16_kernel<128,256,2,2>",
-    "gemm16_kernel<128,128,2,2>", "gemm16s_kernel", "gemm_kernel<64,64,2,2,4>",
+    "gemm16_kernel<128,128,2,2>", "gemm16_kernel<128,224,2,2>", "gemm16s_kernel",
+    "gemm_kernel<64,64,2,2,4>",
     "gemm_kernel<64,128,2,2,4>", "gemm_kernel<128,128,2,2,4>", "gemm_kernel<32,64,1,2,4>",
 }
 # The split-K forms of ptpc_gemm_ws: 128x128 tiles of the 32x32x64 kernel

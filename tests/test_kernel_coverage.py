@@ -14,7 +14,8 @@ import parity_shapes
 GEMM_KERNELS = {
     "gemm16_kernel<256,256,2,2>", "gemm16_kernel<192,256,2,2>", "gemm16_kernel<256,224,4,1>",
     "gemm16_kernel<256,160,2,2>", "gemm16_kernel<128,256,2,2>",
-    "gemm16_kernel<128,128,2,2>", "gemm16s_kernel", "gemm_kernel<64,64,2,2,4>",
+    "gemm16_kernel<128,128,2,2>", "gemm16_kernel<128,224,2,2>", "gemm16s_kernel",
+    "gemm_kernel<64,64,2,2,4>",
     "gemm_kernel<64,128,2,2,4>", "gemm_kernel<128,128,2,2,4>", "gemm_kernel<32,64,1,2,4>",
     "gemm_decode_kernel<2,2,4,4>", "gemm_decode_kernel<2,1,4,4>",
     "gemm_decode_kernel<1,2,4,4>", "gemm_decode_kernel<1,1,4,4>",
@@ -66,3 +67,10 @@ def test_queries_reject_what_the_calls_reject(sg):
     assert sg.gemm_kernel(16, (1 << 17) + 16, 512) is None
     assert sg.quant_act_kernel(0, 256) is None
     assert sg.quant_act_kernel(3, 0) == "fill_f32_kernel"
+
+
+def test_lds_poison_shapes_reach_every_pipelined_kernel(sg):
+    """The LDS-poison comparison (a GPU test) runs one shape per pipelined
+    kernel; the choice those shapes make is checked here, on the CPU."""
+    import test_gpu_lds_poison as poison
+    assert {sg.gemm_kernel(*s) for s in poison.SHAPES} == poison.PIPELINED
