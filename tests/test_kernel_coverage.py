@@ -74,3 +74,12 @@ def test_lds_poison_shapes_reach_every_pipelined_kernel(sg):
     kernel; the choice those shapes make is checked here, on the CPU."""
     import test_gpu_lds_poison as poison
     assert {sg.gemm_kernel(*s) for s in poison.SHAPES} == poison.PIPELINED
+
+
+def test_random_parity_shapes_reach_many_kernels(sg):
+    """The seeded random-shape parity test (a GPU test) draws a fixed set of
+    shapes; on the CPU: it reaches most GEMM kernel families, and some of
+    its shapes make the workspace call split K."""
+    import test_gpu_random_shapes as rnd
+    assert len({sg.gemm_kernel(*s) for s in rnd.SHAPES}) >= 9
+    assert sum(sg.gemm_ws_splits(*s) > 1 for s in rnd.SHAPES) >= 2
