@@ -163,7 +163,7 @@ def traffic_record(fetch_csv, write_csv, workload, copy_mb, kind):
     fetch = f["kernel"] * 1024.0 * f_factor
     write = w["kernel"] * 1024.0 * w_factor
     prof = (f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {{c}} --output-format csv "
-            f"-d $REPO/gpurun_out/prof_{{d}} -o p -- python -u $REPO/bench.py --steps 3 "
+            f"-d $OUT/prof_{{d}} -o p -- python -u $REPO/bench.py --steps 3 "
             f"--warmup 1 --no-cpu-baseline --no-judged --only {kind} "
             f"--copy-calibration-mb {copy_mb}")
     return {"workload": workload, "source_sha256_16": source_hash(kind),
@@ -175,8 +175,8 @@ def traffic_record(fetch_csv, write_csv, workload, copy_mb, kind):
             "bytes_per_launch": fetch + write,
             "commands": [
                 prof.format(c="FETCH_SIZE", d="fetch"), prof.format(c="WRITE_SIZE", d="write"),
-                "python bench.py --traffic-from $REPO/gpurun_out/prof_fetch/p_counter_collection.csv "
-                f"$REPO/gpurun_out/prof_write/p_counter_collection.csv --copy-calibration-mb "
+                "python bench.py --traffic-from $OUT/prof_fetch/p_counter_collection.csv "
+                f"$OUT/prof_write/p_counter_collection.csv --copy-calibration-mb "
                 f"{copy_mb} --traffic-kernel {kind}"],
             "note": ("Counters in KiB per dispatch, averaged over the kernel's launches (inputs "
                      "rotating over copies larger than the memory-side cache); each scaled by "
@@ -518,7 +518,7 @@ def sweep(args):
 
 
 # ---------------------------------------------------------------------------
-# the judged shapes: the other large layers the targets are quoted on
+# the other large layer shapes the performance targets are quoted on
 # ---------------------------------------------------------------------------
 def judged_shapes(stream, only=None):
     """The fused GEMM and the activation quantizer on the 70B layers at 1024
