@@ -239,10 +239,17 @@ static int pow2_ceil(int64_t v) {
 // spills) reads X once where the two-pass kernel reads it twice: rows of
 // 40960-65536 elements went from 3.2-3.4 to 6.0-6.2 TB/s.  Reachable shapes:
 // G = 16 with VPT 1..8 (up to 128 vectors), G = 32 with VPT 8 (129..255
-// vectors), G = 256 with VPT 1..32, and the long-row kernel.
+// vectors), G = 256 with VPT 1 or 2 (256..512 vectors), G = 128 with VPT 8
+// (513..1024), G = 256 with VPT 8..32 (1025..8192), and the long-row kernel.
 ActPlan act_plan(int64_t Ci) {
     const int64_t nchunk = Ci / 8;
     int64_t G = 256;
+    // Rows of 513..1024 vectors: two rows per workgroup, 8 vectors per
+    // thread instead of 4 (8192 tokens, each input streamed from HBM: rows of
+    // 6144 elements 65.7 -> 68.9% of HBM, rows of 8192 69.1 -> 69.7% and
+    // 69.9 -> 71.4% in two runs; 16 vectors per thread, for longer rows, was
+    // 2-3% slower, and rows of 4096 elements lost).
+    if (nchunk > 512 && nchunk <= 1024) G = 128;
     if (nchunk < 256) {
         G = pow2_ceil((nchunk + 7) / 8);
         if (G < 16) G = 16;
@@ -265,6 +272,7 @@ const char* quant_act_plan_name(int64_t T, int64_t Ci) {
     const int lv = __builtin_ctz((unsigned)p.vpt);
     if (p.G == 16) return names[lv];
     if (p.G == 32) return names[4];
+    if (p.G == 128) return "quant_act_kernel<128,8>";
     return names[5 + lv];
 }
 

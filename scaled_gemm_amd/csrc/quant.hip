@@ -94,15 +94,15 @@ __global__ __launch_bounds__(256) void quant_act_kernel(
     const float d = scale_from_amax(__uint_as_float(amax_bits << 16));
     const Divisor dv = make_divisor(d);
     uint2* qr = reinterpret_cast<uint2*>(qx + t * ldq);
-    // Rows of 256 or more vectors store their codes with the non-temporal
-    // hint: 4-8% faster with every input and output streamed from HBM (rows
-    // of 4096-28672 elements); with an output buffer the memory-side cache
-    // already holds, it was 0.5-4% slower.
+    // Rows of 256 or more vectors (128 or 256 threads per row) store their
+    // codes with the non-temporal hint: 4-8% faster with every input and
+    // output streamed from HBM (rows of 4096-28672 elements); with an output
+    // buffer the memory-side cache already holds, it was 0.5-4% slower.
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
         const int64_t c = (int64_t)j * G + g;
         if (c < nchunk) {
-            if constexpr (G == 256)
+            if constexpr (G >= 128)
                 store_nt(qr + c, quantize8(v[j], dv));
             else
                 qr[c] = quantize8(v[j], dv);
@@ -178,10 +178,10 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t Ci, int64_t ld
         }
     }
     if (p.G == 32) return launch_act<32, 8>(x, T, Ci, ldx, qx, ldq, dx, s);
+    if (p.G == 128) return launch_act<128, 8>(x, T, Ci, ldx, qx, ldq, dx, s);
     switch (p.vpt) {
         case 1: return launch_act<256, 1>(x, T, Ci, ldx, qx, ldq, dx, s);
         case 2: return launch_act<256, 2>(x, T, Ci, ldx, qx, ldq, dx, s);
-        case 4: return launch_act<256, 4>(x, T, Ci, ldx, qx, ldq, dx, s);
         case 8: return launch_act<256, 8>(x, T, Ci, ldx, qx, ldq, dx, s);
         case 16: return launch_act<256, 16>(x, T, Ci, ldx, qx, ldq, dx, s);
         default: return launch_act<256, 32>(x, T, Ci, ldx, qx, ldq, dx, s);

@@ -23,7 +23,7 @@ GEMM_KERNELS = {
 ACT_KERNELS = {
     "quant_act_kernel<16,1>", "quant_act_kernel<16,2>", "quant_act_kernel<16,4>",
     "quant_act_kernel<16,8>", "quant_act_kernel<32,8>", "quant_act_kernel<256,1>",
-    "quant_act_kernel<256,2>", "quant_act_kernel<256,4>", "quant_act_kernel<256,8>",
+    "quant_act_kernel<256,2>", "quant_act_kernel<128,8>", "quant_act_kernel<256,8>",
     "quant_act_kernel<256,16>", "quant_act_kernel<256,32>", "quant_act_long_kernel",
 }
 
