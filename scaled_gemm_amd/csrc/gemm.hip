@@ -32,13 +32,14 @@
 // that belongs in its fixed LDS slot.
 //
 // Kernels: gemm16_kernel (tiled, 128..256-row x 128..256-column tiles,
-// 16x16x128 MFMAs), gemm16s_kernel (64x64 tiles of 65..128 tokens, the K
+// 16x16x128 MFMAs; also the two-range split of 256x256 tiles, joined inside
+// the kernel), gemm16s_kernel (64x64 tiles of 65..128 tokens, the K
 // steps split between the waves, each on its own LDS ring), gemm_kernel
 // (tiled, 32x64 and 64-row tiles -- also from 256 tokens where 128x128 tiles
 // would leave CUs idle -- and the split-K form, 32x32x64 MFMAs),
 // gemm_decode_kernel (up to 64 tokens: K split across the waves of a
 // workgroup, operands loaded straight into registers), and the second
-// passes of the two-step forms and of split-K.
+// passes of the two-step forms and of split-K with more than two ranges.
 #include <mutex>
 #include <utility>
 
