@@ -14,6 +14,9 @@ branch:
     accumulator registers within the previous 6 wait states.
 
 Both windows are several times the wait states a 16x16x128 MFMA needs.
+
+The same assembly also shows that no GEMM kernel spills registers inside its
+K loop (a spill there would reload from memory between MFMAs).
 """
 import os
 import re
@@ -192,3 +195,54 @@ def test_lds_poison_build_writes_its_poison(gemm_asm):
     assert len(piped) >= 18          # fused and two-step forms of every tiled kernel
     for n in piped:
         assert poi[n] > rel[n], (n, rel[n], poi[n])
+
+
+def _kernels(asm):
+    """(name, instructions, private bytes per lane) of every kernel in the file."""
+    for m in re.finditer(r"\n(_ZN4ptpc\w+):", asm):
+        end = asm.find(".Lfunc_end", m.start())
+        if end < 0:
+            continue
+        ins = [line.split(";")[0].strip() for line in asm[m.start():end].split("\n")[1:]]
+        ins = [line for line in ins if line and not line.startswith(".")]
+        meta = re.search(r"\.amdhsa_kernel " + re.escape(m.group(1)) + r"\n(.*?)\.end_amdhsa_kernel",
+                         asm, re.S)
+        priv = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", meta.group(1)).group(1))
+        yield m.group(1), ins, priv
+
+
+def _spills_inside(ins):
+    """Scratch accesses between the first and the last MFMA of a kernel."""
+    mfma = [k for k, line in enumerate(ins) if line.startswith("v_mfma")]
+    if not mfma:
+        return []
+    return [ins[k] for k in range(mfma[0], mfma[-1] + 1) if ins[k].startswith("scratch_")]
+
+
+def test_no_spills_in_k_loops(gemm_asm):
+    """Every GEMM kernel's accumulators and operand registers fit: no scratch
+    (spill) access between a kernel's first and last MFMA, that is inside its
+    K loop and remainder steps, and at most 128 bytes of private memory per
+    lane anywhere (the two-range join keeps a few accumulator slabs there
+    while it waits for the other range, after its K loop)."""
+    asm = gemm_asm["release"]
+    seen = 0
+    for name, ins, priv in _kernels(asm):
+        seen += 1
+        assert priv <= 128, (name, priv)
+        inside = _spills_inside(ins)
+        assert not inside, (name, inside[:4])
+    assert seen >= 30
+
+
+def test_spill_check_catches_a_planted_spill():
+    """The scan above on a synthetic kernel: a spill between two MFMAs is
+    found, one after the last MFMA is not."""
+    body = ("\n_ZN4ptpc1xEv:\n\tv_mfma_f32_16x16x128_f8f6f4 a[0:3], v[8:15], v[16:23], a[0:3]\n"
+            "\tscratch_store_dwordx4 off, a[4:7], off\n"
+            "\tv_mfma_f32_16x16x128_f8f6f4 a[0:3], v[8:15], v[16:23], a[0:3]\n"
+            "\tscratch_store_dwordx4 off, a[8:11], off\n.Lfunc_end0:\n"
+            ".amdhsa_kernel _ZN4ptpc1xEv\n\t.amdhsa_private_segment_fixed_size 32\n.end_amdhsa_kernel\n")
+    ((name, ins, priv),) = list(_kernels(body))
+    assert priv == 32
+    assert _spills_inside(ins) == ["scratch_store_dwordx4 off, a[4:7], off"]
