@@ -949,6 +949,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
     float* const tslot = FIXUP ? part + (int64_t)tile_lin * BM * BN : part;
     const __amdgpu_buffer_rsrc_t rpart =
         make_rsrc(tslot, FIXUP ? (uint32_t)(BM * BN * sizeof(float)) : 0u);
+    uint32_t fix_lost = 0;      // the other range's flag never came: NaN output
     if constexpr (FIXUP) {
         // Two K ranges per tile, joined without a second pass.  Each
         // workgroup takes a ticket on its tile's record once its K loop is
@@ -965,8 +966,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
         // does not depend on which range arrives first (IEEE addition
         // commutes): the result is range 0 + range 1 in any timing.  The wait
         // is bounded (kFixupSpins sleeps of ~64 clocks) so that no fault
-        // elsewhere can keep the kernel from exiting.  Records are 4 words
-        // per tile after the slots, cleared before the launch.
+        // elsewhere can keep the kernel from exiting; should it run out, the
+        // tile's outputs are written as NaN instead of a sum with stale
+        // partials.  Records are 4 words per tile after the slots, cleared
+        // before the launch.
         uint32_t* const rec = reinterpret_cast<uint32_t*>(part + (int64_t)ntiles * BM * BN) +
                               4 * tile_lin;
         volatile uint32_t* const bcast = reinterpret_cast<volatile uint32_t*>(b_s2);
@@ -994,8 +997,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
             while (__hip_atomic_load(rec + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
                    ++spins < kFixupSpins)
                 __builtin_amdgcn_s_sleep(1);
+            bcast[1] = __hip_atomic_load(rec + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
         }
         __syncthreads();
+        fix_lost = __builtin_amdgcn_readfirstlane(bcast[1]);
     }
 
     // Epilogue.  The weight slab is the MFMA's first operand, so the 16x16
@@ -1026,6 +1031,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
         for (int i = 0; i < MT; ++i) {
             const int64_t row = m0 + wm * WTM + i * 16 + l16;
             sxv[i] = (scale_mode == kUnitScales || row >= T) ? 1.0f : dx[scale_mode ? 0 : row];
+            if constexpr (FIXUP) sxv[i] = fix_lost ? __builtin_nanf("") : sxv[i];
         }
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
