@@ -155,7 +155,8 @@ size_t ptpc_gemm_workspace_bytes(int64_t T, int64_t Ci, int64_t Co);
  * second pass: of the two workgroups of a tile, the one that finishes first
  * publishes its sums in the workspace, the other adds them to its own and
  * applies the epilogue (per-tile counters in the workspace, cleared by the
- * call; a workgroup only ever waits for one that is already running).  The
+ * call; a workgroup only ever waits for one that is already running, and
+ * its wait is bounded: sums that never arrive leave that tile NaN).  The
  * result is deterministic and the same in both forms; it can differ from
  * ptpc_gemm's in the last bf16 bit (another fp32 summation order).
  * PTPC_ERR_NULL for a missing, PTPC_ERR_SHAPE for a too small workspace.
