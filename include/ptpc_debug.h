@@ -15,6 +15,12 @@
  *       [0] workgroup start, [1] K loop entered (first operands landed),
  *       [2] K loop done, [3] last output store completed.
  *     Same ABI plus the call below; results equal libptpc.so's.
+ *
+ * libptpc_join_lost.so  (-DPTPC_JOIN_LOST) The two-range K join of
+ *     ptpc_gemm_ws / ptpc_gemm_noalloc never raises its per-tile flag and
+ *     waits only 16 sleeps for it, so every joined tile takes the path of a
+ *     wait that runs out: its outputs are NaN.  Every other path equals
+ *     libptpc.so bit for bit.
  */
 #ifndef PTPC_DEBUG_H
 #define PTPC_DEBUG_H

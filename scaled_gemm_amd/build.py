@@ -23,6 +23,9 @@ POISON_LIB = os.path.join(PKG, "libptpc_lds_poison.so")
 # (start, K loop entered, K loop done, stores done) into a buffer set with
 # ptpc_debug_set_timeline (bench.py --timeline).
 TIMELINE_LIB = os.path.join(PKG, "libptpc_timeline.so")
+# Debug variant: the two-range K join never raises its flag and waits only a
+# few sleeps, so every joined tile takes the path of a wait that runs out.
+JOIN_LOST_LIB = os.path.join(PKG, "libptpc_join_lost.so")
 
 SOURCES = ["ptpc_api.cpp", "plan.cpp", "quant.hip", "gemm.hip"]
 
@@ -50,7 +53,8 @@ def _variant(name, defines):
     """(objects, compile commands, link command) of one build variant."""
     out_dir = os.path.join(BUILD, name)
     os.makedirs(out_dir, exist_ok=True)
-    lib = {"release": LIB, "lds_poison": POISON_LIB, "timeline": TIMELINE_LIB}[name]
+    lib = {"release": LIB, "lds_poison": POISON_LIB, "timeline": TIMELINE_LIB,
+           "join_lost": JOIN_LOST_LIB}[name]
     objs, cmds = [], []
     for src in SOURCES:
         obj = os.path.join(out_dir, src.replace(".", "_") + ".o")
@@ -63,9 +67,10 @@ def _variant(name, defines):
 
 
 def build(verbose: bool = False) -> str:
-    """Build libptpc.so and its two debug variants."""
+    """Build libptpc.so and its three debug variants."""
     variants = [_variant("release", []), _variant("lds_poison", ["-DPTPC_LDS_POISON"]),
-                _variant("timeline", ["-DPTPC_TIMELINE"])]
+                _variant("timeline", ["-DPTPC_TIMELINE"]),
+                _variant("join_lost", ["-DPTPC_JOIN_LOST"])]
     cmds = [c for _, cs, _ in variants for c in cs]
     with ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for out in ex.map(lambda c: _run(c, verbose), cmds):

@@ -52,8 +52,16 @@ constexpr int BK = 64;          // K bytes per step (one MFMA K step)
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // Bound on the sleeps of the two-range fix-up's wait (gemm16_kernel): about
 // 2^20 x 64 clocks, far beyond the microseconds the other range needs to
-// publish its sums.
+// publish its sums.  The lost-flag debug build (-DPTPC_JOIN_LOST,
+// libptpc_join_lost.so) never raises the flag and waits 16 sleeps, so that
+// every joined tile takes the path of a wait that runs out.
+#ifdef PTPC_JOIN_LOST
+constexpr int kFixupSpins = 16;
+constexpr bool kRaiseJoinFlag = false;
+#else
 constexpr int kFixupSpins = 1 << 20;
+constexpr bool kRaiseJoinFlag = true;
+#endif
 // Cache-policy bits of a buffer load: sc1, device-coherent (reads memory,
 // not a stale line of this XCD's L2).
 constexpr int kSc1 = 16;
@@ -988,7 +996,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm16_kernel(
             // write-back that the flag's release makes
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            if (tid == 0)
+            if (tid == 0 && kRaiseJoinFlag)
                 __hip_atomic_store(rec + 1, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
